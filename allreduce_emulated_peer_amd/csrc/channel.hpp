@@ -1,0 +1,131 @@
+// MemoryChannel-style device layer for R emulated ranks on one GPU.
+//
+// Semantics follow the channel methods described for MSCCL++ (README, Key
+// Concepts, "On-GPU Communication Interfaces: Channels" and "PortChannel and
+// MemoryChannel"):
+//   put(dstOffset, srcOffset, size)  copy `size` bytes from local memory at
+//                                    srcOffset to the peer's memory at
+//                                    dstOffset (offsets and size in bytes);
+//                                    a MemoryChannel does it with many GPU
+//                                    threads loading and storing directly.
+//   get                              the reverse direction: read the peer's
+//                                    memory directly.
+//   signal()                         tell the peer "I have arrived and all my
+//                                    earlier memory operations are done".
+//   flush()                          make earlier channel operations complete
+//                                    from the local device's point of view.
+//   wait()                           block until the peer has signalled.
+//   barrier                          signal, (flush,) wait, then a local
+//                                    workgroup barrier so the other local
+//                                    threads are synchronised too.
+//
+// On one GPU a "peer's memory" is another buffer in the same HBM, reached by
+// ordinary global loads and stores; the rank boundary that matters is the
+// workgroup boundary (and, across the 8 XCDs, separate L2 caches).  A
+// channel therefore connects (rank r, slot b) with (rank p, slot b): slot b is
+// the b-th workgroup of each rank.  Its semaphore is a 32-bit counter in
+// global memory, inbound[r][p][b], counting signals rank p's slot b has sent
+// to rank r's slot b.  Counters only grow; the number of signals a slot has
+// already consumed is kept per (rank, slot) in device memory (not in kernel
+// arguments), so repeated launches and replays of a captured graph wait for
+// the right epoch.  Comparisons are wrap-safe.
+//
+// Memory ordering across XCDs: signal is an agent-scope release atomic add
+// (the compiler emits an L2 write-back before it), wait spins on agent-scope
+// relaxed loads (which bypass the non-coherent caches) and ends with an
+// agent-scope acquire fence (L1/L2 invalidate).  Waits are bounded by a
+// wall-clock budget; on expiry the kernel records MSCL_ERR_TIMEOUT in the
+// host-mapped status word and carries on, so no wave is ever left spinning.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.hpp"
+
+namespace mscl {
+
+constexpr int kMaxRanks = 16;
+constexpr int kStatusTimeout = 7;  // MSCL_ERR_TIMEOUT
+
+// Channel state of one launch, passed by value in the kernel arguments.
+struct ChannelArgs {
+  uint32_t* inbound;       // [R][R][slots] signal counters
+  uint32_t* consumed;      // [R][slots] signals consumed per peer so far
+  int* status;             // host-mapped status word
+  uint32_t slots;          // slot stride of inbound / consumed
+  int32_t drop_rank;       // test control: this rank skips signal(); -1 = none
+  uint64_t timeout_ticks;  // bound of one wait(), in wall-clock ticks (100 MHz)
+};
+
+// The channels of rank `rank`'s slot `slot` to all of its peers.
+struct RankChannels {
+  const ChannelArgs& ch;
+  int nranks;
+  int rank;
+  int slot;
+
+  __device__ uint32_t* inbound_from(int peer) const {
+    return ch.inbound + (static_cast<uint64_t>(rank) * nranks + peer) * ch.slots + slot;
+  }
+  __device__ uint32_t* inbound_of(int peer) const {  // the peer's counter for signals from us
+    return ch.inbound + (static_cast<uint64_t>(peer) * nranks + rank) * ch.slots + slot;
+  }
+
+  // signal(): release-ordered increment of the peer's inbound counter.
+  __device__ void signal(int peer) const {
+    if (rank == ch.drop_rank) return;
+    __hip_atomic_fetch_add(inbound_of(peer), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // flush(): earlier stores complete from this device's point of view.
+  __device__ static void flush() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+  // wait(): until the peer's signal count reaches `epoch`; false on timeout.
+  __device__ bool wait(int peer, uint32_t epoch) const {
+    const uint32_t* c = inbound_from(peer);
+    const uint64_t start = wall_clock64();
+    while (static_cast<int32_t>(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch) < 0) {
+      if (wall_clock64() - start > ch.timeout_ticks) {
+        __hip_atomic_store(ch.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+  }
+
+  // Barrier of this slot with the same slot of every peer.  Executed by the
+  // whole workgroup.  Lane p of wave 0 drives the channel to peer p, so the
+  // R-1 signals and waits of a slot go out as one vector instruction each.
+  __device__ void barrier_all() const {
+    __syncthreads();  // every local thread's earlier accesses are done
+    if (threadIdx.x < 64) {
+      const int peer = threadIdx.x;
+      uint32_t* consumed = ch.consumed + static_cast<uint64_t>(rank) * ch.slots + slot;
+      // vector (atomic) accesses: the counter is rewritten inside the kernel
+      const uint32_t epoch = __hip_atomic_load(consumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
+      const bool active = peer < nranks && peer != rank;
+      if (active) signal(peer);
+      if (active) wait(peer, epoch);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (peer == 0) __hip_atomic_store(consumed, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();  // the rest of the workgroup is now synchronised with the peers
+  }
+};
+
+// put() at lane granularity: vector `vi` of this rank's buffer `src` is
+// written to the same vector offset of every peer's buffer.  A workgroup
+// whose lanes cover consecutive vectors performs the pages' cooperative
+// put(dstOffset, srcOffset, size) to all R-1 peers at once, reading the
+// source once instead of once per peer.
+template <class C, int R>
+__device__ inline void put_to_peers(void* const* dst, int rank, uint64_t vi, const u32x4& v,
+                                    uint64_t nfull, int ntail) {
+#pragma unroll
+  for (int p = 0; p < R; ++p)
+    if (p != rank) store_any<C>(dst[p], vi, v, nfull, ntail);
+}
+
+}  // namespace mscl

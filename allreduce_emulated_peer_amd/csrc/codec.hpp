@@ -1,0 +1,153 @@
+// 16-byte vector I/O and element codecs for gfx950.
+//
+// Every rank buffer is moved in 16-byte vectors (one global_load_dwordx4 /
+// global_store_dwordx4 per lane, 1 KiB per wavefront instruction, fully
+// coalesced).  A vector holds V = 16 / sizeof(element) elements.  Elements are
+// widened to binary32 exactly and the binary32 totals are rounded back with
+// the hardware's round-to-nearest-even conversions:
+//   bf16 -> f32 : 16-bit shift (exact)
+//   f16  -> f32 : v_cvt_f32_f16 (exact, subnormals kept)
+//   f32  -> bf16: v_cvt_pk_bf16_f32 (gfx950; RNE, NaN stays NaN)
+//   f32  -> f16 : v_cvt_f16_f32 (RNE, subnormals kept, overflow to Inf)
+// The partial vector at the end of a rank's range is handled element by
+// element so that no access goes past the buffer.
+//
+// Vector lanes are always copied into a scalar before __builtin_bit_cast:
+// bit-casting a subscripted ext_vector element directly reads lane 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscl {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct F32 {
+  static constexpr int kElemBytes = 4;
+  static constexpr int V = 4;
+  __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      f[i] = __builtin_bit_cast(float, w);
+    }
+  }
+  __device__ static inline u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = f[i];
+      v[i] = __builtin_bit_cast(uint32_t, x);
+    }
+    return v;
+  }
+};
+
+struct BF16 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int V = 8;
+  __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static inline u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 pair = {f[2 * i], f[2 * i + 1]};
+      const bf16x2 h = __builtin_convertvector(pair, bf16x2);
+      v[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return v;
+  }
+};
+
+struct F16 {
+  static constexpr int kElemBytes = 2;
+  static constexpr int V = 8;
+  __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      const f16x2 h = __builtin_bit_cast(f16x2, w);
+      f[2 * i] = (float)h[0];
+      f[2 * i + 1] = (float)h[1];
+    }
+  }
+  __device__ static inline u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 pair = {f[2 * i], f[2 * i + 1]};
+      const f16x2 h = __builtin_convertvector(pair, f16x2);
+      v[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return v;
+  }
+};
+
+// Full 16-byte vector `vi` of a buffer.
+__device__ inline u32x4 load_vec(const void* base, uint64_t vi) {
+  return reinterpret_cast<const u32x4*>(base)[vi];
+}
+__device__ inline void store_vec(void* base, uint64_t vi, const u32x4& v) {
+  reinterpret_cast<u32x4*>(base)[vi] = v;
+}
+
+// First `nvalid` (< V) elements of vector `vi`; the rest read as zero bits.
+template <class C>
+__device__ inline u32x4 load_partial(const void* base, uint64_t vi, int nvalid) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if constexpr (C::kElemBytes == 4) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(base) + vi * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nvalid) v[k] = p[k];
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + vi * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nvalid) v[k >> 1] |= static_cast<uint32_t>(p[k]) << (16 * (k & 1));
+  }
+  return v;
+}
+
+// Store only the first `nvalid` (< V) elements of vector `vi`.
+template <class C>
+__device__ inline void store_partial(void* base, uint64_t vi, const u32x4& v, int nvalid) {
+  if constexpr (C::kElemBytes == 4) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(base) + vi * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nvalid) p[k] = v[k];
+  } else {
+    uint16_t* p = reinterpret_cast<uint16_t*>(base) + vi * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nvalid) p[k] = static_cast<uint16_t>(v[k >> 1] >> (16 * (k & 1)));
+  }
+}
+
+// Vector `vi` of a range holding `nfull` full vectors followed by a partial
+// vector of `ntail` elements.
+template <class C>
+__device__ inline u32x4 load_any(const void* base, uint64_t vi, uint64_t nfull, int ntail) {
+  if (vi < nfull) return load_vec(base, vi);
+  return load_partial<C>(base, vi, ntail);
+}
+template <class C>
+__device__ inline void store_any(void* base, uint64_t vi, const u32x4& v, uint64_t nfull, int ntail) {
+  if (vi < nfull)
+    store_vec(base, vi, v);
+  else
+    store_partial<C>(base, vi, v, ntail);
+}
+
+}  // namespace mscl

@@ -1,0 +1,672 @@
+// MemoryChannel-style AllReduce over R emulated peer ranks on one gfx950 GPU.
+//
+// The MSCCL++ pages present AllReduce as the collective their library speeds
+// up for tensor-parallel LLM serving (project summary, "Highlighted
+// Details"), built from GPU-side channel methods (README, Key Concepts,
+// "On-GPU Communication Interfaces: Channels") of which the MemoryChannel
+// moves data with many GPU threads loading and storing peer memory directly
+// ("PortChannel and MemoryChannel").  This file holds the two kernels and the
+// host side of the C ABI declared in include/mscl.h.
+//
+// Rank layout.  Workgroup w of a launch is emulated rank (w % R), channel
+// slot (w / R); with the hardware's round-robin dispatch of workgroups over
+// the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.  Each
+// workgroup has 256 threads (4 wavefronts of 64); each thread keeps U
+// 16-byte vectors of each of the R rank buffers in flight per iteration.
+//
+// One-shot: every rank reads all R inputs over the whole buffer, reduces in
+// registers (binary32, rank order) and writes its own output.  When an output
+// is also an input (in place), the ranks' slot-b workgroups run the channel
+// barrier between their loads and their stores of each tile, because a
+// rank's stores overwrite an input its peers are still reading.
+//
+// Two-shot: rank r owns chunk r = elements [r*c, min((r+1)*c, n)) with
+// c = roundup(ceil(n/R), V).  Reduce-scatter: rank r reads chunk r of all R
+// inputs and writes the reduced chunk to its own output.  Then the channel
+// barrier (signal every peer, wait for every peer).  All-gather: rank r puts
+// its reduced chunk into every peer's output, reading it back in reverse
+// tile order so the most recently written tiles are still in cache.  Each
+// thread handles the same vectors in both phases, which keeps in-place calls
+// safe: the only reader of in[p][chunk r] is rank r itself, earlier in the
+// same thread.
+//
+// Both kernels add in rank order 0..R-1 starting from rank 0's value and
+// round once, so their results are bit-identical to each other.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/mscl.h"
+#include "channel.hpp"
+#include "codec.hpp"
+
+namespace mscl {
+
+constexpr int kThreads = 256;
+
+// 16-byte vectors per thread per rank buffer per iteration: R*U loads in
+// flight per thread (16 for R >= 4) without running out of VGPRs.
+template <int R>
+constexpr int unroll_for() {
+  return R <= 4 ? 4 : (R <= 8 ? 2 : 1);
+}
+
+struct KernelArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t count;  // elements per rank buffer
+  uint64_t chunk;  // two-shot: elements per rank chunk, a multiple of V
+  uint32_t nblk;   // workgroups (slots) per rank in this launch
+  ChannelArgs ch;
+};
+
+// binary32 sum of one 16-byte vector position over the R ranks, in rank
+// order starting from rank 0's value, rounded once to the element type.
+template <class C, int R>
+__device__ inline u32x4 reduce_vec(const u32x4 (&x)[R]) {
+  float acc[C::V];
+  C::unpack(x[0], acc);
+#pragma unroll
+  for (int p = 1; p < R; ++p) {
+    float t[C::V];
+    C::unpack(x[p], t);
+#pragma unroll
+    for (int i = 0; i < C::V; ++i) acc[i] = acc[i] + t[i];
+  }
+  return C::pack(acc);
+}
+
+// The partial vector at the end of the buffer (n % V elements), reduced by
+// a single thread.
+template <class C, int R>
+__device__ inline u32x4 reduce_partial(const KernelArgs& a, uint64_t vi, int ntail) {
+  u32x4 x[R];
+#pragma unroll
+  for (int p = 0; p < R; ++p) x[p] = load_partial<C>(a.in[p], vi, ntail);
+  return reduce_vec<C, R>(x);
+}
+
+// A tile is U*256 consecutive 16-byte vectors: lane l of the workgroup takes
+// vectors base+l, base+256+l, ... so each wavefront instruction covers 1 KiB
+// contiguous.  Full tiles (kFull) need no bounds checks, which keeps every
+// load of the tile issued back to back; the last, partial tile re-reads the
+// range's last vector in lanes past the end and skips their stores.
+template <int R, int U, bool kFull>
+__device__ inline void load_tile(u32x4 (&x)[U][R], const void* const* src, uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
+#pragma unroll
+    for (int p = 0; p < R; ++p) x[u][p] = load_vec(src[p], vi);
+  }
+}
+
+template <int U, bool kFull>
+__device__ inline void store_tile(void* dst, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (kFull || vi < vend) store_vec(dst, vi, y[u]);
+  }
+}
+
+template <class C, int R, int U>
+__device__ inline void reduce_tile(u32x4 (&y)[U], const u32x4 (&x)[U][R]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) y[u] = reduce_vec<C, R>(x[u]);
+}
+
+// One tile of the one-shot: all R inputs -> own output, with the channel
+// barrier between loads and stores when running in place.
+template <class C, int R, int U, bool kInPlace, bool kFull>
+__device__ inline void oneshot_tile(const KernelArgs& a, const RankChannels& chans, void* dst, uint64_t base,
+                                    uint64_t vend) {
+  u32x4 x[U][R];
+  u32x4 y[U];
+  load_tile<R, U, kFull>(x, a.in, base, vend);
+  reduce_tile<C, R, U>(y, x);
+  if constexpr (kInPlace) chans.barrier_all();
+  store_tile<U, kFull>(dst, y, base, vend);
+}
+
+template <class C, int R, bool kInPlace>
+__global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
+  constexpr int V = C::V;
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t n = a.count;
+  const uint64_t nfull = n / V;
+  const int ntail = static_cast<int>(n % V);
+  const uint64_t ntiles = (nfull + kTile - 1) / kTile;
+  const RankChannels chans{a.ch, R, rank, slot};
+  void* const dst = a.out[rank];
+
+  for (uint64_t t = slot; t < ntiles; t += a.nblk) {
+    const uint64_t base = t * kTile + threadIdx.x;
+    if ((t + 1) * kTile <= nfull)
+      oneshot_tile<C, R, U, kInPlace, true>(a, chans, dst, base, nfull);
+    else
+      oneshot_tile<C, R, U, kInPlace, false>(a, chans, dst, base, nfull);
+  }
+
+  if (ntail != 0 && slot == 0) {
+    u32x4 y = {0u, 0u, 0u, 0u};
+    if (threadIdx.x == 0) y = reduce_partial<C, R>(a, nfull, ntail);
+    if constexpr (kInPlace) chans.barrier_all();
+    if (threadIdx.x == 0) store_partial<C>(dst, nfull, y, ntail);
+  }
+}
+
+template <class C, int R, int U, bool kFull>
+__device__ inline void rs_tile(const KernelArgs& a, void* mine, uint64_t base, uint64_t vend) {
+  u32x4 x[U][R];
+  u32x4 y[U];
+  load_tile<R, U, kFull>(x, a.in, base, vend);  // get() from every peer
+  reduce_tile<C, R, U>(y, x);
+  store_tile<U, kFull>(mine, y, base, vend);
+}
+
+template <class C, int R, int U, bool kFull>
+__device__ inline void ag_tile(const KernelArgs& a, int rank, const void* mine, uint64_t base, uint64_t vend) {
+  u32x4 y[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
+    y[u] = load_vec(mine, vi);
+  }
+#pragma unroll
+  for (int p = 0; p < R; ++p)  // put() to every peer
+    if (p != rank) store_tile<U, kFull>(a.out[p], y, base, vend);
+}
+
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
+  constexpr int V = C::V;
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t n = a.count;
+  const uint64_t lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, n);
+  const uint64_t hi = std::min<uint64_t>(lo + a.chunk, n);
+  const uint64_t v_lo = lo / V;    // chunk starts are multiples of V
+  const uint64_t v_full = hi / V;  // end of the chunk's full vectors
+  // nonzero only for the non-empty chunk that holds the buffer's end
+  const int ntail = hi > lo ? static_cast<int>(hi % V) : 0;
+  const uint64_t nv = v_full - v_lo;
+  const uint64_t ntiles = (nv + kTile - 1) / kTile;
+  const RankChannels chans{a.ch, R, rank, slot};
+  void* const mine = a.out[rank];
+
+  // Reduce-scatter: chunk `rank` of every input -> own output.
+  for (uint64_t t = slot; t < ntiles; t += a.nblk) {
+    const uint64_t base = v_lo + t * kTile + threadIdx.x;
+    if ((t + 1) * kTile <= nv)
+      rs_tile<C, R, U, true>(a, mine, base, v_full);
+    else
+      rs_tile<C, R, U, false>(a, mine, base, v_full);
+  }
+  const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
+  if (tail_owner) store_partial<C>(mine, v_full, reduce_partial<C, R>(a, v_full, ntail), ntail);
+
+  // signal / wait with the same slot of every peer rank.
+  chans.barrier_all();
+
+  // All-gather: put the reduced chunk into every peer's output, newest
+  // tiles first.  Same lanes, same vectors as the reduce-scatter.
+  if (ntiles > static_cast<uint64_t>(slot)) {
+    const uint64_t last = slot + (ntiles - 1 - slot) / a.nblk * a.nblk;
+    for (uint64_t t = last + a.nblk; t > static_cast<uint64_t>(slot);) {
+      t -= a.nblk;
+      const uint64_t base = v_lo + t * kTile + threadIdx.x;
+      if ((t + 1) * kTile <= nv)
+        ag_tile<C, R, U, true>(a, rank, mine, base, v_full);
+      else
+        ag_tile<C, R, U, false>(a, rank, mine, base, v_full);
+    }
+  }
+  if (tail_owner) {
+    const u32x4 y = load_partial<C>(mine, v_full, ntail);
+    put_to_peers<C, R>(a.out, rank, v_full, y, v_full, ntail);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Kernel tables
+// ----------------------------------------------------------------------------
+
+using KernelFn = void (*)(KernelArgs);
+enum { kAlgoOneShot = 0, kAlgoOneShotInPlace = 1, kAlgoTwoShot = 2, kNumKernelKinds = 3 };
+
+template <class C, int R>
+constexpr KernelFn kernel_for(int kind) {
+  return kind == kAlgoOneShot ? &mscl_oneshot<C, R, false>
+         : kind == kAlgoOneShotInPlace ? &mscl_oneshot<C, R, true>
+                                       : &mscl_twoshot<C, R>;
+}
+
+template <class C, int... Rs>
+KernelFn pick(int kind, int R, std::integer_sequence<int, Rs...>) {
+  KernelFn fn = nullptr;
+  ((R == Rs + 1 ? (fn = kernel_for<C, Rs + 1>(kind), 0) : 0), ...);
+  return fn;
+}
+
+KernelFn kernel_lookup(int kind, int dtype, int R) {
+  auto seq = std::make_integer_sequence<int, kMaxRanks>{};
+  switch (dtype) {
+    case MSCL_FLOAT32: return pick<F32>(kind, R, seq);
+    case MSCL_FLOAT16: return pick<F16>(kind, R, seq);
+    case MSCL_BFLOAT16: return pick<BF16>(kind, R, seq);
+  }
+  return nullptr;
+}
+
+int unroll_for_runtime(int R) { return R <= 4 ? 4 : (R <= 8 ? 2 : 1); }
+
+}  // namespace mscl
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+
+namespace {
+
+using namespace mscl;
+
+thread_local std::string g_last_error;
+
+mscl_status_t fail(mscl_status_t s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+mscl_status_t fail_hip(hipError_t e, const char* what) {
+  return fail(MSCL_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t elem_bytes(int dtype) { return dtype == MSCL_FLOAT32 ? 4 : 2; }
+
+size_t env_size(const char* name, size_t dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  unsigned long long x = strtoull(v, &end, 10);
+  return (end && *end == 0) ? static_cast<size_t>(x) : dflt;
+}
+
+struct Config {
+  size_t oneshot_max_bytes;  // selector threshold on bytes per rank buffer
+  size_t wg_target_total;    // default workgroups per launch (all ranks)
+  size_t wg_per_rank;        // fixed workgroups per rank (0 = automatic)
+  uint64_t wait_timeout_us;  // default bound of one device-side wait
+};
+
+const Config& config() {
+  static Config c;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    c.oneshot_max_bytes = env_size("MSCL_ONESHOT_MAX_BYTES", 64 * 1024);
+    c.wg_target_total = env_size("MSCL_WG_TOTAL", 512);
+    c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
+    c.wait_timeout_us = env_size("MSCL_WAIT_TIMEOUT_MS", 2000) * 1000;
+  });
+  return c;
+}
+
+}  // namespace
+
+struct mscl_channel_s {
+  int device = 0;
+  int nranks = 0;
+  int refcount = 0;
+  int cus = 0;
+  uint32_t slots = 0;            // barrier slots allocated per rank (= max co-resident workgroups per rank)
+  uint64_t wall_clock_khz = 100000;
+  uint32_t* inbound = nullptr;   // device [R][R][slots]
+  uint32_t* consumed = nullptr;  // device [R][slots]
+  int* status_host = nullptr;    // host-mapped status word
+  int* status_dev = nullptr;
+  uint64_t wait_timeout_us = 0;  // 0 = config default
+  int drop_rank = -1;
+};
+
+namespace {
+
+std::mutex g_mutex;
+std::map<std::pair<int, int>, mscl_channel_s*> g_registry;
+
+bool registered(mscl_channel_s* ch) {
+  for (auto& kv : g_registry)
+    if (kv.second == ch) return true;
+  return false;
+}
+
+mscl_status_t validate_call(const void* const inputs[], void* const outputs[], size_t count, int dtype,
+                            int nranks, int algo, bool* in_place) {
+  if (nranks < 1 || nranks > MSCL_MAX_RANKS)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "nranks must be in 1..16");
+  if (dtype != MSCL_FLOAT32 && dtype != MSCL_FLOAT16 && dtype != MSCL_BFLOAT16)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (algo != MSCL_ALGO_AUTO && algo != MSCL_ALGO_ONE_SHOT && algo != MSCL_ALGO_TWO_SHOT)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown algo");
+  if (!inputs || !outputs) return fail(MSCL_ERR_INVALID_ARGUMENT, "inputs/outputs array is null");
+  const size_t e = elem_bytes(dtype);
+  if (count > SIZE_MAX / e) return fail(MSCL_ERR_INVALID_ARGUMENT, "count * element size overflows");
+  const uintptr_t bytes = count * e;
+  *in_place = false;
+  for (int r = 0; r < nranks; ++r) {
+    if (!inputs[r] || !outputs[r]) return fail(MSCL_ERR_INVALID_ARGUMENT, "null buffer pointer");
+    if ((reinterpret_cast<uintptr_t>(inputs[r]) & 15u) || (reinterpret_cast<uintptr_t>(outputs[r]) & 15u))
+      return fail(MSCL_ERR_MISALIGNED, "buffers must be 16-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(inputs[r]);
+    const uintptr_t b = reinterpret_cast<uintptr_t>(outputs[r]);
+    if (UINTPTR_MAX - a < bytes || UINTPTR_MAX - b < bytes)
+      return fail(MSCL_ERR_INVALID_ARGUMENT, "buffer range wraps the address space");
+  }
+  if (count == 0) return MSCL_SUCCESS;
+  auto overlap = [bytes](const void* x, const void* y) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return a < b + bytes && b < a + bytes;
+  };
+  for (int r = 0; r < nranks; ++r) {
+    for (int q = r + 1; q < nranks; ++q)
+      if (overlap(outputs[r], outputs[q])) return fail(MSCL_ERR_INVALID_ARGUMENT, "outputs overlap");
+    for (int p = 0; p < nranks; ++p) {
+      if (p == r && outputs[r] == inputs[r]) {
+        *in_place = true;
+        continue;
+      }
+      if (overlap(outputs[r], inputs[p]))
+        return fail(MSCL_ERR_INVALID_ARGUMENT,
+                    "an output overlaps an input (only outputs[r] == inputs[r] is allowed)");
+    }
+  }
+  return MSCL_SUCCESS;
+}
+
+mscl_algo_t resolve_algo(size_t count, int dtype, int algo) {
+  if (algo != MSCL_ALGO_AUTO) return static_cast<mscl_algo_t>(algo);
+  return count * elem_bytes(dtype) <= config().oneshot_max_bytes ? MSCL_ALGO_ONE_SHOT : MSCL_ALGO_TWO_SHOT;
+}
+
+void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t algo, bool in_place,
+               mscl_plan_t* plan) {
+  const int R = ch->nranks;
+  const uint64_t V = 16 / elem_bytes(dtype);
+  const uint64_t tile = static_cast<uint64_t>(kThreads) * unroll_for_runtime(R);
+  const Config& cfg = config();
+  memset(plan, 0, sizeof(*plan));
+  plan->algo = algo;
+  plan->nranks = R;
+  plan->threads_per_workgroup = kThreads;
+  plan->vectors_per_thread = unroll_for_runtime(R);
+  uint64_t vectors;  // full vectors one rank covers
+  if (algo == MSCL_ALGO_TWO_SHOT) {
+    const uint64_t per = (count + R - 1) / R;
+    const uint64_t c = (per + V - 1) / V * V;
+    plan->chunk_elems = c;
+    vectors = c / V;
+    plan->uses_barrier = 1;
+  } else {
+    vectors = count / V;
+    plan->uses_barrier = in_place ? 1 : 0;
+  }
+  uint64_t want = std::max<uint64_t>(1, (vectors + tile - 1) / tile);
+  uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, cfg.wg_target_total / R);
+  cap = std::min<uint64_t>(cap, ch->slots);  // every workgroup of a barrier must be resident
+  plan->workgroups_per_rank = static_cast<int>(std::min(want, cap));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mscl_version(void) { return MSCL_VERSION_MAJOR * 10000 + MSCL_VERSION_MINOR * 100 + MSCL_VERSION_PATCH; }
+
+const char* mscl_status_string(mscl_status_t s) {
+  switch (s) {
+    case MSCL_SUCCESS: return "success";
+    case MSCL_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MSCL_ERR_UNSUPPORTED: return "unsupported device";
+    case MSCL_ERR_MISALIGNED: return "buffer not 16-byte aligned";
+    case MSCL_ERR_NOT_INITIALIZED: return "no channel set for this device and rank count";
+    case MSCL_ERR_OUT_OF_MEMORY: return "out of memory";
+    case MSCL_ERR_HIP: return "HIP runtime error";
+    case MSCL_ERR_TIMEOUT: return "device-side wait timed out";
+  }
+  return "unknown status";
+}
+
+const char* mscl_last_error_string(void) { return g_last_error.c_str(); }
+
+mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, mscl_algo_t* out) {
+  if (!out) return fail(MSCL_ERR_INVALID_ARGUMENT, "out is null");
+  if (nranks < 1 || nranks > MSCL_MAX_RANKS) return fail(MSCL_ERR_INVALID_ARGUMENT, "nranks must be in 1..16");
+  if (dtype != MSCL_FLOAT32 && dtype != MSCL_FLOAT16 && dtype != MSCL_BFLOAT16)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (count > SIZE_MAX / elem_bytes(dtype)) return fail(MSCL_ERR_INVALID_ARGUMENT, "size overflows");
+  *out = resolve_algo(count, dtype, MSCL_ALGO_AUTO);
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
+  if (!out) return fail(MSCL_ERR_INVALID_ARGUMENT, "out is null");
+  *out = nullptr;
+  if (nranks < 1 || nranks > MSCL_MAX_RANKS) return fail(MSCL_ERR_INVALID_ARGUMENT, "nranks must be in 1..16");
+  if (device < 0) return fail(MSCL_ERR_INVALID_ARGUMENT, "device must be >= 0");
+  std::lock_guard<std::mutex> lock(g_mutex);
+  auto key = std::make_pair(device, nranks);
+  auto it = g_registry.find(key);
+  if (it != g_registry.end()) {
+    it->second->refcount += 1;
+    *out = it->second;
+    return MSCL_SUCCESS;
+  }
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDeviceCount");
+  if (device >= ndev) return fail(MSCL_ERR_INVALID_ARGUMENT, "no such device");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MSCL_ERR_UNSUPPORTED, std::string("this library is built for gfx950, device is ") + prop.gcnArchName);
+  int prev = 0;
+  e = hipGetDevice(&prev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return fail_hip(e, "hipSetDevice");
+
+  auto* ch = new mscl_channel_s();
+  ch->device = device;
+  ch->nranks = nranks;
+  ch->refcount = 1;
+  ch->cus = prop.multiProcessorCount;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+    ch->wall_clock_khz = static_cast<uint64_t>(khz);
+  // Slots: the fewest workgroups per rank that can be resident at once over
+  // every kernel that runs the barrier, so a barrier can never wait on a
+  // workgroup that has not been scheduled.
+  int min_resident = 1 << 30;
+  for (int dt = 0; dt < 3; ++dt) {
+    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot}) {
+      int per_cu = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)),
+                                                       kThreads, 0);
+      if (e != hipSuccess) {
+        delete ch;
+        (void)hipSetDevice(prev);
+        return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+      }
+      min_resident = std::min(min_resident, per_cu * ch->cus);
+    }
+  }
+  ch->slots = static_cast<uint32_t>(std::max(1, std::min(min_resident / nranks, 4096)));
+  const size_t inbound_bytes = sizeof(uint32_t) * nranks * nranks * ch->slots;
+  const size_t consumed_bytes = sizeof(uint32_t) * nranks * ch->slots;
+  mscl_status_t st = MSCL_SUCCESS;
+  if ((e = hipMalloc(&ch->inbound, inbound_bytes)) != hipSuccess ||
+      (e = hipMalloc(&ch->consumed, consumed_bytes)) != hipSuccess) {
+    st = fail(MSCL_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
+  } else if ((e = hipHostMalloc(&ch->status_host, sizeof(int), hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess) {
+    st = fail(MSCL_ERR_OUT_OF_MEMORY, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  } else if ((e = hipHostGetDevicePointer(reinterpret_cast<void**>(&ch->status_dev), ch->status_host, 0)) != hipSuccess) {
+    st = fail_hip(e, "hipHostGetDevicePointer");
+  } else {
+    *ch->status_host = MSCL_SUCCESS;
+    if ((e = hipMemset(ch->inbound, 0, inbound_bytes)) != hipSuccess ||
+        (e = hipMemset(ch->consumed, 0, consumed_bytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess)
+      st = fail_hip(e, "zeroing channel state");
+  }
+  if (st != MSCL_SUCCESS) {
+    if (ch->inbound) (void)hipFree(ch->inbound);
+    if (ch->consumed) (void)hipFree(ch->consumed);
+    if (ch->status_host) (void)hipHostFree(ch->status_host);
+    delete ch;
+    (void)hipSetDevice(prev);
+    return st;
+  }
+  (void)hipSetDevice(prev);
+  g_registry[key] = ch;
+  *out = ch;
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_channel_destroy(mscl_channel_t ch) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+  if (--ch->refcount > 0) return MSCL_SUCCESS;
+  g_registry.erase(std::make_pair(ch->device, ch->nranks));
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(ch->device);
+  hipError_t e1 = hipFree(ch->inbound);
+  hipError_t e2 = hipFree(ch->consumed);
+  hipError_t e3 = hipHostFree(ch->status_host);
+  (void)hipSetDevice(prev);
+  delete ch;
+  if (e1 != hipSuccess) return fail_hip(e1, "hipFree");
+  if (e2 != hipSuccess) return fail_hip(e2, "hipFree");
+  if (e3 != hipSuccess) return fail_hip(e3, "hipHostFree");
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_channel_check(mscl_channel_t ch) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+  const int s = __atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE);
+  if (s != MSCL_SUCCESS) return fail(s, "a device-side wait timed out in an earlier call");
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_channel_reset(mscl_channel_t ch) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(ch->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemset(ch->inbound, 0, sizeof(uint32_t) * ch->nranks * ch->nranks * ch->slots);
+  if (e == hipSuccess) e = hipMemset(ch->consumed, 0, sizeof(uint32_t) * ch->nranks * ch->slots);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail_hip(e, "resetting channel state");
+  __atomic_store_n(ch->status_host, MSCL_SUCCESS, __ATOMIC_RELEASE);
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t ch, uint64_t wait_timeout_us, int drop_signal_rank) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+  if (drop_signal_rank < -1 || drop_signal_rank >= ch->nranks)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "drop_signal_rank must be -1 or a rank");
+  ch->wait_timeout_us = wait_timeout_us;
+  ch->drop_rank = drop_signal_rank;
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_channel_plan(mscl_channel_t ch, size_t count, mscl_dtype_t dtype, mscl_algo_t algo,
+                                int in_place, mscl_plan_t* plan) {
+  if (!plan) return fail(MSCL_ERR_INVALID_ARGUMENT, "plan is null");
+  if (dtype != MSCL_FLOAT32 && dtype != MSCL_FLOAT16 && dtype != MSCL_BFLOAT16)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (algo != MSCL_ALGO_AUTO && algo != MSCL_ALGO_ONE_SHOT && algo != MSCL_ALGO_TWO_SHOT)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown algo");
+  if (count > SIZE_MAX / elem_bytes(dtype)) return fail(MSCL_ERR_INVALID_ARGUMENT, "size overflows");
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+  make_plan(ch, count, dtype, resolve_algo(count, dtype, algo), in_place != 0, plan);
+  return MSCL_SUCCESS;
+}
+
+mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], size_t count, mscl_dtype_t dtype,
+                             int nranks, mscl_algo_t algo, void* stream) {
+  bool in_place = false;
+  mscl_status_t st = validate_call(inputs, outputs, count, dtype, nranks, algo, &in_place);
+  if (st != MSCL_SUCCESS || count == 0) return st;
+
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  mscl_channel_s* ch = nullptr;
+  uint64_t timeout_us;
+  int drop_rank;
+  {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    auto it = g_registry.find(std::make_pair(device, nranks));
+    if (it == g_registry.end())
+      return fail(MSCL_ERR_NOT_INITIALIZED, "call mscl_channel_create for this device and rank count first");
+    ch = it->second;
+    timeout_us = ch->wait_timeout_us ? ch->wait_timeout_us : config().wait_timeout_us;
+    drop_rank = ch->drop_rank;
+  }
+  if (__atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE) != MSCL_SUCCESS)
+    return fail(MSCL_ERR_TIMEOUT, "an earlier call timed out; call mscl_channel_reset");
+
+  const mscl_algo_t resolved = resolve_algo(count, dtype, algo);
+  mscl_plan_t plan;
+  make_plan(ch, count, dtype, resolved, in_place, &plan);
+
+  KernelArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.in[r] = inputs[r];
+    a.out[r] = outputs[r];
+  }
+  a.count = count;
+  a.chunk = plan.chunk_elems;
+  a.nblk = static_cast<uint32_t>(plan.workgroups_per_rank);
+  a.ch.inbound = ch->inbound;
+  a.ch.consumed = ch->consumed;
+  a.ch.status = ch->status_dev;
+  a.ch.slots = ch->slots;
+  a.ch.drop_rank = drop_rank;
+  a.ch.timeout_ticks = timeout_us * ch->wall_clock_khz / 1000;
+
+  int kind = resolved == MSCL_ALGO_TWO_SHOT ? kAlgoTwoShot : (in_place ? kAlgoOneShotInPlace : kAlgoOneShot);
+  KernelFn fn = kernel_lookup(kind, dtype, nranks);
+  if (!fn) return fail(MSCL_ERR_INVALID_ARGUMENT, "no kernel for this dtype and rank count");
+  const dim3 grid(static_cast<unsigned>(nranks * plan.workgroups_per_rank));
+  void* kargs[] = {&a};
+  e = hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(kThreads), kargs, 0,
+                      static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return MSCL_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the emulated-peer AllReduce on one MI355X.
+
+One step = one mscl_allreduce call (algorithm chosen by size: two-shot at
+this size — reduce-scatter, signal/wait barrier, all-gather put) over R = 8
+emulated ranks of 128 MiB bf16 buffers each (8192 tokens x 8192 hidden,
+N(0, 0.5)), inputs already resident in HBM.  Prints ONE JSON line:
+
+  value          algbw = S / t  (S = bytes per rank buffer, t = time per step)
+  pct_hbm_peak   (2*R*S / t) / 8 TB/s  -- R*S read plus R*S written
+  roofline       the two-shot kernel: algorithmic bytes 2*R*S per launch over
+                 its mean launch duration from HIP events on the launch stream;
+                 `traffic` from the committed rocprofv3 counter summary
+  cpu_baseline   the plain-C oracle on the host cores, on a bounded sample
+  latency        p50 of per-call time at 16 KiB (R=8 bf16; R=4 fp32) and the
+                 512 KiB decode-shaped case
+
+Options: --gpus N (only 1: the emulation runs on one GPU), --steps K,
+--warmup W, --no-cpu-baseline, --sweep (per-size table to stderr),
+--copy-calibration (also run a plain 1 GiB device copy, for counter scaling).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AllReduce algbw GB/s + % of HBM peak, R=8 bf16, 512KB–128MB; p50 µs at 16KB"
+HBM_PEAK_GBPS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "twoshot_bf16_r8_128MiB_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "allreduce_emulated_peer_amd", "csrc", f)
+                  for f in ("mscl.hip", "channel.hpp", "codec.hpp")]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken on different kernel sources."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--latency-iters", type=int, default=1000)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: the R emulated ranks all live on one GPU, "
+              "and this build runs no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from allreduce_emulated_peer_amd import mscl as M
+    from allreduce_emulated_peer_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    M.load()  # raises if the HIP library is missing
+    dev = torch.cuda.current_device()
+    stream = torch.cuda.current_stream()
+
+    def device_inputs(w):
+        xs = W.generate_all(w)
+        tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        out = []
+        for x in xs:
+            t = torch.from_numpy(x.view(np.int16) if w.dtype == "bf16" else x)
+            out.append((t.view(torch.bfloat16) if w.dtype == "bf16" else t).to("cuda"))
+            assert out[-1].dtype == tdt
+        del xs
+        return out
+
+    code = {"fp32": M.FLOAT32, "fp16": M.FLOAT16, "bf16": M.BFLOAT16}
+
+    def caller(w, ins, outs, algo=M.ALGO_AUTO):
+        M.channel_create(w.nranks, dev)
+        ip = [t.data_ptr() for t in ins]
+        op = [t.data_ptr() for t in outs]
+        lib = M.load()
+        import ctypes
+        in_arr = (ctypes.c_void_p * w.nranks)(*ip)
+        out_arr = (ctypes.c_void_p * w.nranks)(*op)
+        s = ctypes.c_void_p(stream.cuda_stream)
+        n, dt, R = w.count, code[w.dtype], w.nranks
+
+        def call():
+            st = lib.mscl_allreduce(in_arr, out_arr, n, dt, R, algo, s)
+            if st != M.SUCCESS:
+                raise M.MsclError(st, "mscl_allreduce", M.last_error_string())
+        return call
+
+    def p50_us(call, iters):
+        for _ in range(20):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+        return float(np.median(t)), float(t.mean())
+
+    # ---------------------------------------------------------------- main
+    w = W.prefill_bf16()
+    log(f"[bench] generating {w.name}: R={w.nranks} x {w.bytes_per_rank} B")
+    ins = device_inputs(w)
+    outs = [torch.empty_like(t) for t in ins]
+    call = caller(w, ins, outs)
+    plan = M.channel_plan(M.channel_create(w.nranks, dev), w.count, M.BFLOAT16, M.ALGO_AUTO)
+    algo_name = {1: "one_shot", 2: "two_shot"}[plan.algo]
+    log(f"[bench] plan: {algo_name}, {plan.workgroups_per_rank} workgroups/rank x {plan.threads_per_workgroup} "
+        f"threads, {plan.vectors_per_thread} vectors/thread")
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1000.0 / args.steps
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    S = w.bytes_per_rank
+    alg_bytes = w.algorithmic_bytes
+    algbw = S / (ms_per_step / 1000.0) / 1e9
+    hbm_gbps = alg_bytes / (ms_per_step / 1000.0) / 1e9
+    achieved = alg_bytes / (kern_ms.mean() / 1000.0) / 1e9
+    log(f"[bench] {ms_per_step:.4f} ms/step wall, kernel mean {kern_ms.mean():.4f} ms (p50 {np.median(kern_ms):.4f}),"
+        f" algbw {algbw:.1f} GB/s, {hbm_gbps:.1f} GB/s algorithmic HBM ({100 * hbm_gbps / HBM_PEAK_GBPS:.1f}% of peak)")
+    traffic = committed_traffic()
+    roofline = {"bound": "hbm", "kernel": f"mscl_twoshot<BF16, 8>", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
+                "mean_launch_ms": round(float(kern_ms.mean()), 5)}
+    del ins, outs
+    torch.cuda.empty_cache()
+
+    # --------------------------------------------------- latency + decode
+    latency = {}
+    for lw in (W.sweep_bf16(14), W.integer_small()):
+        li = device_inputs(lw)
+        lo = [torch.empty_like(t) for t in li]
+        p50, mean = p50_us(caller(lw, li, lo), args.latency_iters)
+        latency[f"p50_us_16KiB_{lw.name}"] = round(p50, 2)
+        log(f"[bench] {lw.name}: p50 {p50:.2f} us, mean {mean:.2f} us per call")
+    dw = W.decode_bf16()
+    di = device_inputs(dw)
+    do = [torch.empty_like(t) for t in di]
+    p50, mean = p50_us(caller(dw, di, do), args.latency_iters)
+    decode = {"workload": dw.name, "p50_us": round(p50, 2), "algbw_GBps_p50": round(dw.bytes_per_rank / p50 / 1e3, 1),
+              "cache": "hot (8 MiB footprint stays in cache)"}
+    log(f"[bench] {dw.name}: p50 {p50:.2f} us, algbw {decode['algbw_GBps_p50']} GB/s")
+    del di, do
+
+    if args.sweep:
+        log("[bench] sweep R=8 bf16 (hot buffers): size, algo, p50 us, algbw GB/s, % HBM peak")
+        for k in range(10, 28):
+            sw = W.sweep_bf16(k)
+            si = device_inputs(sw)
+            so = [torch.empty_like(t) for t in si]
+            for algo, name in ((M.ALGO_ONE_SHOT, "one_shot"), (M.ALGO_TWO_SHOT, "two_shot")):
+                iters = 200 if sw.bytes_per_rank <= (1 << 20) else (50 if sw.bytes_per_rank <= (32 << 20) else 20)
+                p50, _ = p50_us(caller(sw, si, so, algo), iters)
+                log(f"[sweep] {sw.bytes_per_rank:>10d} {name:>8s} {p50:10.2f} {sw.bytes_per_rank / p50 / 1e3:8.1f} "
+                    f"{100 * sw.algorithmic_bytes / p50 / 1e3 / HBM_PEAK_GBPS:6.1f}")
+            del si, so
+            torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 plain copies of {nbytes} bytes")
+        del src, dst
+
+    # ---------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import cpu as C
+
+        cores = min(os.cpu_count() or 1, 16)
+        n_sample = 1 << 24  # first 16 Mi elements (32 MiB) of each of the 8 rank buffers
+        xs = [W.generate(w, r)[:n_sample].copy() for r in range(w.nranks)]
+        outs_h = [np.empty(n_sample, dtype=np.uint16) for _ in range(w.nranks)]
+        C.allreduce(xs, "bf16", nthreads=cores, outputs=outs_h)  # warm
+        reps, t_total = 0, 0.0
+        while t_total < 10.0 and reps < 50:
+            t1 = time.perf_counter()
+            C.allreduce(xs, "bf16", nthreads=cores, outputs=outs_h)
+            t_total += time.perf_counter() - t1
+            reps += 1
+        t_per = t_total / reps
+        cpu = {"value": round(n_sample * 2 / t_per / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"plain-C oracle, first {n_sample} elements of each of the 8 rank buffers of {w.name}, "
+                         f"{reps} runs, {t_per * 1000:.1f} ms per run; same algbw accounting (S/t)"}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s algbw on {cores} threads")
+
+    line = {
+        "metric": METRIC, "value": round(algbw, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "nranks": w.nranks, "elements_per_rank": w.count,
+                   "bytes_per_rank": S, "accumulate": "f32", "algo": f"auto -> {algo_name}",
+                   "workgroups_per_rank": plan.workgroups_per_rank, "parallelism": "8 emulated ranks on 1 GPU"},
+        "pct_hbm_peak": round(100 * hbm_gbps / HBM_PEAK_GBPS, 2),
+        "hbm_gbps_algorithmic": round(hbm_gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "latency": latency,
+        "decode_512KiB": decode,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

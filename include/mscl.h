@@ -1,0 +1,200 @@
+/*
+ * mscl.h — C ABI of a MemoryChannel-style AllReduce over R emulated peer
+ * ranks held in one AMD Instinct MI355X (gfx950).
+ *
+ * What is emulated.  The MSCCL++ pages describe a peer-to-peer connection
+ * between two GPUs (a "channel") that is built on the host, copied to the GPU
+ * at initialisation, and used from kernel code through device functions
+ * put / get / signal / flush / wait (MSCCL++ README, Key Concepts, "On-GPU
+ * Communication Interfaces: Channels").  A MemoryChannel moves data with GPU
+ * threads reading and writing the peer's memory directly (same page,
+ * "PortChannel and MemoryChannel").  The pages' collective library offers
+ * AllReduce for tensor-parallel serving (MSCCL++ project summary,
+ * "Highlighted Details"; MSCCL++ ASPLOS'26 abstract).  Here the R ranks are
+ * R groups of workgroups of one kernel, each rank's "remote" memory is a
+ * buffer in the same GPU's HBM, and the channel semaphores are counters in
+ * global memory.
+ *
+ * Result.  Every output buffer receives the element-wise sum of all R input
+ * buffers, accumulated in binary32 in rank order 0..R-1 starting from rank
+ * 0's value, then rounded once to the element type with round-to-nearest-even
+ * (subnormals kept, NaN/Inf propagated).  The pages fix no accumulation rule;
+ * this is the reading taken, and it makes one-shot and two-shot results
+ * bit-identical to each other.
+ *
+ * Threading.  Calls on one channel set (one device, one R) share its
+ * semaphores, so they must be ordered on one stream (or otherwise
+ * serialised); different channel sets are independent.  The registry itself
+ * is thread-safe.
+ *
+ * Errors.  Every entry point returns a status code and never aborts.  The
+ * text of the last failure on the calling thread is available from
+ * mscl_last_error_string().  Argument validation runs on the host before any
+ * HIP call.
+ */
+#ifndef MSCL_H
+#define MSCL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSCL_MAX_RANKS 16
+#define MSCL_VERSION_MAJOR 0
+#define MSCL_VERSION_MINOR 1
+#define MSCL_VERSION_PATCH 0
+
+typedef enum {
+  MSCL_FLOAT32 = 0,  /* IEEE binary32 */
+  MSCL_FLOAT16 = 1,  /* IEEE binary16 */
+  MSCL_BFLOAT16 = 2  /* bfloat16 (upper half of a binary32 pattern) */
+} mscl_dtype_t;
+
+typedef enum {
+  MSCL_ALGO_AUTO = 0,     /* one-shot up to a size threshold, two-shot above it */
+  MSCL_ALGO_ONE_SHOT = 1, /* every rank reads all R inputs and writes its own output */
+  MSCL_ALGO_TWO_SHOT = 2  /* reduce-scatter, device barrier, all-gather put */
+} mscl_algo_t;
+
+typedef int mscl_status_t;
+#define MSCL_SUCCESS 0
+#define MSCL_ERR_INVALID_ARGUMENT 1 /* a null/overlapping pointer, bad R, dtype, algo or size */
+#define MSCL_ERR_UNSUPPORTED 2      /* the device is not a gfx950 GPU */
+#define MSCL_ERR_MISALIGNED 3       /* a buffer is not 16-byte aligned */
+#define MSCL_ERR_NOT_INITIALIZED 4  /* no channel set exists for (current device, R) */
+#define MSCL_ERR_OUT_OF_MEMORY 5    /* channel state could not be allocated */
+#define MSCL_ERR_HIP 6              /* a HIP runtime call or kernel launch failed */
+#define MSCL_ERR_TIMEOUT 7          /* a device-side wait() ran out of time */
+
+typedef struct mscl_channel_s* mscl_channel_t;
+
+/* Launch geometry chosen for one call (for tests and tooling). */
+typedef struct {
+  mscl_algo_t algo;          /* resolved algorithm (never AUTO) */
+  int nranks;                /* R */
+  int workgroups_per_rank;   /* B: workgroups (channel slots) per emulated rank */
+  int threads_per_workgroup; /* 256 */
+  int vectors_per_thread;    /* 16-byte vectors each thread keeps in flight per rank buffer */
+  int uses_barrier;          /* 1 when the kernel runs the signal/wait barrier */
+  size_t chunk_elems;        /* two-shot: elements owned by each rank (a multiple of 16/elem_size) */
+} mscl_plan_t;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int mscl_version(void);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char* mscl_status_string(mscl_status_t status);
+
+/* Text describing the most recent failure on the calling thread ("" if none). */
+const char* mscl_last_error_string(void);
+
+/*
+ * Create (or reference) the channel set for `nranks` emulated ranks on HIP
+ * device `device`.
+ *   nranks : 1..MSCL_MAX_RANKS.
+ *   device : HIP device ordinal; must be a gfx950 GPU.
+ *   out    : receives the handle (non-null).
+ * The host builds the channel state once and the kernels receive it by value
+ * at launch — the pages' "constructed by host-side interfaces and copied to
+ * GPUs during initialization" (MSCCL++ README, Key Concepts, Channels).  State
+ * owned by the library: per (receiver rank, sender rank, slot) semaphore
+ * counters and per (rank, slot) consumed-signal counters in device memory, a
+ * status word in host-mapped memory, and the slot count derived from the
+ * kernels' occupancy so that every workgroup taking part in a barrier is
+ * resident at once.  A second create for the same (device, nranks) returns
+ * the same handle with its reference count raised.  Leaves the current
+ * device unchanged.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, OUT_OF_MEMORY, HIP.
+ */
+mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out);
+
+/*
+ * Drop one reference; the state is freed when the count reaches zero.  The
+ * caller must have synchronised every stream that used the set.
+ * Errors: INVALID_ARGUMENT (null or unknown handle), HIP.
+ */
+mscl_status_t mscl_channel_destroy(mscl_channel_t channel);
+
+/*
+ * Report a device-side failure recorded by an earlier call on this set
+ * (currently only a wait() timeout).  Reads the host-mapped status word; it
+ * does not synchronise, so synchronise the stream first for a complete
+ * answer.  Returns SUCCESS or the recorded code (TIMEOUT).
+ */
+mscl_status_t mscl_channel_check(mscl_channel_t channel);
+
+/*
+ * Zero the semaphores, the consumed-signal counters and the status word
+ * (synchronous; the device must be idle on this set).  Needed after a
+ * TIMEOUT, whose missing signals leave the counters out of step.
+ * Errors: INVALID_ARGUMENT, HIP.
+ */
+mscl_status_t mscl_channel_reset(mscl_channel_t channel);
+
+/*
+ * AllReduce (sum) over R emulated ranks.
+ *   inputs  : host array of nranks device pointers; inputs[r] is rank r's
+ *             buffer of `count` elements.  Read only.  Inputs may alias each
+ *             other.
+ *   outputs : host array of nranks device pointers; outputs[r] receives the
+ *             reduced buffer (count elements).  outputs[r] may equal
+ *             inputs[r] (in place); otherwise it must not overlap any input,
+ *             and no two outputs may overlap.
+ *   count   : elements per buffer; 0 is a no-op that launches nothing.
+ *   dtype   : element type of inputs and outputs.
+ *   nranks  : R, 1..MSCL_MAX_RANKS; a channel set for (current device, R)
+ *             must exist (mscl_channel_create).
+ *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT or _TWO_SHOT.  All give bit-identical
+ *             results.
+ *   stream  : hipStream_t on the current device (NULL = default stream).
+ * Every pointer must be 16-byte aligned and on the current device.  The call
+ * is asynchronous: it validates, launches one kernel on `stream` and
+ * returns.  The caller owns all buffers and keeps them alive until the stream
+ * has finished.  Nothing is allocated or copied to the device per call: the
+ * pointer tables travel in the kernel arguments.
+ * A TIMEOUT recorded by an earlier call makes this call return TIMEOUT
+ * without launching, until mscl_channel_reset().
+ * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
+ */
+mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], size_t count,
+                             mscl_dtype_t dtype, int nranks, mscl_algo_t algo, void* stream);
+
+/*
+ * The algorithm MSCL_ALGO_AUTO resolves to for this size: one-shot when the
+ * per-rank buffer (count * element size) is at most the one-shot threshold,
+ * else two-shot.  Pure host computation.  The threshold can be overridden
+ * with the environment variable MSCL_ONESHOT_MAX_BYTES (read once).
+ * Errors: INVALID_ARGUMENT.
+ */
+mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, mscl_algo_t* out);
+
+/*
+ * The launch geometry mscl_allreduce would use on this channel set for this
+ * size and algorithm (in_place: 1 if any outputs[r] == inputs[r]).  Pure host
+ * computation.  Errors: INVALID_ARGUMENT.
+ */
+mscl_status_t mscl_channel_plan(mscl_channel_t channel, size_t count, mscl_dtype_t dtype,
+                                mscl_algo_t algo, int in_place, mscl_plan_t* plan);
+
+/*
+ * Failure-handling controls for tests (never needed in normal use).
+ *   wait_timeout_us : bound on every device-side wait() of later calls on
+ *                     this set, in microseconds (0 restores the default of
+ *                     MSCL_WAIT_TIMEOUT_MS or 2000 ms).
+ *   drop_signal_rank: -1 for normal operation; r in 0..R-1 makes rank r skip
+ *                     its signal() in later calls, so its peers' wait()s run
+ *                     into the bound and record TIMEOUT.  Every kernel still
+ *                     exits.
+ * Errors: INVALID_ARGUMENT.
+ */
+mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t channel, uint64_t wait_timeout_us,
+                                              int drop_signal_rank);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSCL_H */

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: exports, validation codes, the selector.
+
+Every call here fails validation (or is pure host logic) before the library
+makes any HIP call, so nothing touches a device.
+"""
+
+import os
+import re
+
+import pytest
+
+from allreduce_emulated_peer_amd import mscl as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mscl.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mscl_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = M.load()
+    decl = declared_functions()
+    assert len(decl) >= 11
+    for name in decl:
+        assert hasattr(lib, name), f"{name} declared in mscl.h but not exported"
+    assert sorted(M.EXPORTS) == decl
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import importlib
+
+    mod = importlib.reload(M)
+    try:
+        mod._lib = None
+        with pytest.raises(FileNotFoundError):
+            mod.load(str(tmp_path / "nope.so"))
+    finally:
+        importlib.reload(M)
+
+
+def test_version_and_strings():
+    assert M.version() == 100
+    for code in range(8):
+        assert M.status_string(code) != "unknown status"
+    assert M.status_string(99) == "unknown status"
+
+
+A = 0x100000  # aligned fake addresses: never dereferenced (validation fails or count == 0)
+
+
+def addrs(R, base, step=0x10000000):
+    return [base + r * step for r in range(R)]
+
+
+@pytest.mark.parametrize("R", [0, -1, 17])
+def test_bad_nranks(R):
+    assert M.raw_allreduce(addrs(1, A), addrs(1, A * 2), 10, M.BFLOAT16, R, 0, 0) == M.ERR_INVALID_ARGUMENT
+
+
+def test_bad_dtype_and_algo():
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 3, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, -1, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 3, 0) == M.ERR_INVALID_ARGUMENT
+
+
+def test_null_arrays_and_pointers():
+    assert M.raw_allreduce(None, addrs(2, A), 10, 0, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), None, 10, 0, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+    ins = addrs(2, A)
+    ins[1] = 0
+    assert M.raw_allreduce(ins, addrs(2, A * 64), 10, 0, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+    assert "null" in M.last_error_string()
+
+
+def test_misaligned():
+    ins = addrs(4, A)
+    ins[2] += 8
+    assert M.raw_allreduce(ins, addrs(4, A * 64), 10, 0, 4, 0, 0) == M.ERR_MISALIGNED
+    outs = addrs(4, A * 64)
+    outs[3] += 2
+    assert M.raw_allreduce(addrs(4, A), outs, 10, 0, 4, 0, 0) == M.ERR_MISALIGNED
+
+
+def test_overlaps():
+    n = 1024  # fp32: 4 KiB per buffer
+    ins = addrs(3, A, step=0x1000)
+    # outputs overlapping each other
+    outs = [A * 64, A * 64 + 0x800, A * 64 + 0x2000]
+    assert M.raw_allreduce(ins, outs, n, 0, 3, 0, 0) == M.ERR_INVALID_ARGUMENT
+    # an output overlapping another rank's input
+    outs = [A * 64, ins[2], A * 64 + 0x4000]
+    assert M.raw_allreduce(ins, outs, n, 0, 3, 0, 0) == M.ERR_INVALID_ARGUMENT
+    # an output partially overlapping its own input
+    outs = [ins[0] + 0x10, A * 64, A * 64 + 0x4000]
+    assert M.raw_allreduce(ins, outs, n, 0, 3, 0, 0) == M.ERR_INVALID_ARGUMENT
+    # in place but inputs alias, so the in-place output overlaps another input
+    ins2 = [A, A, A + 0x1000]
+    outs = [A, A * 64, A * 64 + 0x4000]
+    assert M.raw_allreduce(ins2, outs, n, 0, 3, 0, 0) == M.ERR_INVALID_ARGUMENT
+
+
+def test_count_zero_is_a_noop():
+    assert M.raw_allreduce(addrs(8, A), addrs(8, A * 64), 0, M.BFLOAT16, 8, 0, 0) == M.SUCCESS
+
+
+def test_size_overflow():
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 2 ** 63, M.FLOAT32, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 2 ** 62, M.FLOAT32, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
+
+
+def test_selector():
+    # one-shot up to the threshold (64 KiB per rank buffer by default), two-shot above
+    assert M.select_algo(1, M.BFLOAT16, 8) == M.ALGO_ONE_SHOT
+    assert M.select_algo(32 * 1024, M.BFLOAT16, 8) == M.ALGO_ONE_SHOT
+    assert M.select_algo(32 * 1024 + 1, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
+    assert M.select_algo(16 * 1024, M.FLOAT32, 4) == M.ALGO_ONE_SHOT
+    assert M.select_algo(64 * 1024 * 1024, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
+    with pytest.raises(M.MsclError):
+        M.select_algo(10, 7, 8)
+    with pytest.raises(M.MsclError):
+        M.select_algo(10, M.FLOAT32, 0)
+
+
+def test_channel_calls_reject_unknown_handles():
+    lib = M.load()
+    import ctypes
+
+    bogus = ctypes.c_void_p(0x1234)
+    assert lib.mscl_channel_destroy(None) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_destroy(bogus) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_check(bogus) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_reset(bogus) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_set_fault_controls(bogus, 0, -1) == M.ERR_INVALID_ARGUMENT
+    plan = M.Plan()
+    assert lib.mscl_channel_plan(bogus, 10, 0, 0, 0, ctypes.byref(plan)) == M.ERR_INVALID_ARGUMENT
+    out = ctypes.c_void_p()
+    assert lib.mscl_channel_create(0, 0, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_create(17, 0, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_create(4, -1, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_create(4, 0, None) == M.ERR_INVALID_ARGUMENT

@@ -1,0 +1,316 @@
+"""GPU parity: the HIP AllReduce (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact for every dtype (ulp distance 0, NaNs as NaN) — stricter than
+the 1-ulp contract for 16-bit types, because the kernels follow the oracle's
+order and rounding exactly — and all R outputs identical.  Covers the five
+reference workloads at full size, tiny brute-force sweeps (R = 1..16, ragged
+lengths, n < R, special values), in-place calls, non-default streams,
+repeated calls (semaphore epochs), graph capture/replay and the bounded-wait
+failure path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as G
+import oracle_pins as P
+from allreduce_emulated_peer_amd import mscl as M
+from allreduce_emulated_peer_amd import workloads as W
+from oracle import allreduce as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    M.load()
+    yield
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "auto"])
+def test_integer_workload_exact(algo):
+    w = W.integer_small()
+    xs = W.generate_all(w)
+    G.note(f"{w.name} {algo}")
+    outs = G.run(xs, "fp32", algo)
+    want = np.sum(np.stack([x.astype(np.float64) for x in xs]), axis=0)
+    got = outs[0].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want), "integer sums must be exact"
+    G.assert_matches_oracle(outs, O.allreduce(xs, "fp32"), "fp32", w.name)
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "auto"])
+def test_decode_bf16(algo):
+    w = W.decode_bf16()
+    xs = W.generate_all(w)
+    G.note(f"{w.name} {algo}")
+    outs = G.run(xs, "bf16", algo)
+    G.assert_matches_oracle(outs, O.allreduce(xs, "bf16"), "bf16", w.name)
+
+
+TINY_COUNTS = (1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 1000, 4097)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_tiny_brute_force(dtype):
+    """R = 1..16, ragged lengths (every residue mod the vector width, n < R),
+    special values mixed in, both algorithms, out of place and in place."""
+    g = np.random.default_rng(4242)
+    specials = P.special_patterns(dtype)
+    for R in range(1, 17):
+        for n in TINY_COUNTS:
+            xs = P.rand_inputs(R, n, dtype, seed=R * 1000 + n, scale=8.0)
+            bitsx = [P.bits_of(x, dtype).copy() for x in xs]
+            for b in bitsx:
+                m = g.random(n) < 0.05
+                b[m] = g.choice(specials, size=int(m.sum()))
+            xs = [P.from_bits(b, dtype) for b in bitsx]
+            want = O.allreduce(xs, dtype)
+            for algo in ("one_shot", "two_shot"):
+                for in_place in (False, True):
+                    G.note(f"tiny {dtype} R={R} n={n} {algo} in_place={in_place}")
+                    outs = G.run(xs, dtype, algo, in_place=in_place)
+                    G.assert_matches_oracle(outs, want, dtype, f"{dtype} R={R} n={n} {algo} ip={in_place}")
+
+
+def test_hand_cases_on_gpu():
+    """The hand-derived golden cases (double rounding, order, signed zero,
+    Inf/NaN, overflow, subnormals) through both kernels."""
+    for dtype, ins, want in P.load_hand_cases():
+        xs = [P.from_bits(np.array([v] * 37), dtype) for v in ins]  # 37: full vectors + a tail
+        for algo in ("one_shot", "two_shot"):
+            G.note(f"hand case {dtype} {[hex(v) for v in ins]} {algo}")
+            outs = G.run(xs, dtype, algo)
+            got = G.to_host_bits(outs[0], dtype)
+            G.assert_outputs_equal_each_other(outs)
+            if want == "nan":
+                assert all(P.decode(int(v), dtype)[0] == "nan" for v in got)
+            else:
+                assert np.all(got == int(want, 16)), f"{dtype} {ins} {algo}: {hex(int(got[0]))} != {want}"
+
+
+@pytest.mark.parametrize("algo", ["auto", "one_shot"])
+def test_prefill_bf16_full(algo):
+    w = W.prefill_bf16()
+    xs = W.generate_all(w)
+    want = O.allreduce(xs, "bf16")
+    G.note(f"{w.name} {algo} (plan {M.channel_plan(G.channel(8), w.count, M.BFLOAT16, G.ALGOS[algo]).workgroups_per_rank} wg/rank)")
+    outs = G.run(xs, "bf16", algo)
+    G.assert_matches_oracle_on_device(outs, want, "bf16", w.name)
+
+
+@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot"])
+def test_ragged_outliers_full(algo):
+    w = W.ragged_outliers_bf16()
+    xs = W.generate_all(w)
+    want = O.allreduce(xs, "bf16")
+    G.note(f"{w.name} {algo}")
+    outs = G.run(xs, "bf16", algo)
+    G.assert_matches_oracle_on_device(outs, want, "bf16", w.name)
+    # the last rank's chunk ends in a 7-element partial vector
+    assert w.count % 8 == 7
+
+
+def test_fp16_sweep():
+    """1 KiB .. 256 MiB per buffer, R = 8, both algorithms.  Up to 16 MiB the
+    whole result is compared with the oracle; above, 64 Ki sampled elements
+    (plus both ends) are, and the two algorithms must agree bit for bit on
+    every element."""
+    for k in range(10, 29):
+        w = W.sweep_fp16(k)
+        xs = W.generate_all(w)
+        dev_in = [G.to_device(x, "fp16") for x in xs]
+        res = {}
+        for algo in ("one_shot", "two_shot"):
+            G.note(f"{w.name} {algo}")
+            res[algo] = G.run(xs, "fp16", algo, dev_inputs=dev_in)
+        if k <= 24:
+            want = O.allreduce(xs, "fp16")
+            for algo, outs in res.items():
+                G.assert_matches_oracle(outs, want, "fp16", f"{w.name} {algo}")
+        else:
+            idx = G.sample_indices(w.count, seed=k)
+            want = O.allreduce_elements(xs, "fp16", idx)
+            for algo, outs in res.items():
+                G.assert_outputs_equal_each_other(outs)
+                got = G.to_host_bits(outs[0], "fp16")[idx]
+                assert np.array_equal(got, want.view(np.uint16)), f"{w.name} {algo}: sampled mismatch"
+            for r in range(8):
+                assert torch.equal(res["one_shot"][r].view(torch.uint8), res["two_shot"][r].view(torch.uint8))
+        del dev_in, res
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot"])
+@pytest.mark.parametrize("R,n,dtype", [(8, 3 * 256 * 2 * 8 * 64 + 5, "bf16"), (16, 1_000_003, "bf16"),
+                                       (4, 777_777, "fp32"), (3, 1 << 20, "fp16"), (8, 9_437_185, "fp16")])
+def test_in_place(algo, R, n, dtype):
+    xs = P.rand_inputs(R, n, dtype, seed=n % 997)
+    want = O.allreduce(xs, dtype)
+    G.note(f"in place R={R} n={n} {dtype} {algo}")
+    outs = G.run(xs, dtype, algo, in_place=True)
+    G.assert_matches_oracle(outs, want, dtype, f"in place R={R} n={n} {algo}")
+
+
+def test_mixed_in_place_and_out_of_place():
+    R, n = 6, 123_457
+    xs = P.rand_inputs(R, n, "bf16", seed=5)
+    want = O.allreduce(xs, "bf16")
+    for algo in ("one_shot", "two_shot"):
+        ins = [G.to_device(x, "bf16") for x in xs]
+        outs = [ins[r] if r % 2 == 0 else G.poison_like(ins[r]) for r in range(R)]
+        G.channel(R)
+        G.note(f"mixed in-place {algo}")
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, G.ALGOS[algo],
+                    torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        G.assert_matches_oracle(outs, want, "bf16", f"mixed in place {algo}")
+
+
+def test_non_default_stream():
+    w = W.decode_bf16()
+    xs = W.generate_all(w)
+    want = O.allreduce(xs, "bf16")
+    s = torch.cuda.Stream()
+    for algo in ("one_shot", "two_shot"):
+        G.note(f"side stream {algo}")
+        outs = G.run(xs, "bf16", algo, stream=s)
+        G.assert_matches_oracle(outs, want, "bf16", f"side stream {algo}")
+
+
+def test_repeated_calls_keep_epochs():
+    """10^4 back-to-back barrier launches: every semaphore epoch must line up
+    (a mismatch would time out and be reported, or give wrong data)."""
+    R, n = 8, 300_001
+    xs = P.rand_inputs(R, n, "bf16", seed=17)
+    want = O.allreduce(xs, "bf16")
+    ins = [G.to_device(x, "bf16") for x in xs]
+    outs = [G.poison_like(t) for t in ins]
+    h = G.channel(R)
+    stream = torch.cuda.current_stream().cuda_stream
+    G.note("10^4 repeated two-shot / in-place one-shot calls")
+    for i in range(10_000):
+        algo = M.ALGO_TWO_SHOT if i % 3 else M.ALGO_ONE_SHOT
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, algo, stream)
+        if i % 1000 == 999:
+            torch.cuda.synchronize()
+            assert M.channel_check(h) == M.SUCCESS
+    torch.cuda.synchronize()
+    assert M.channel_check(h) == M.SUCCESS
+    G.assert_matches_oracle(outs, want, "bf16", "after 10^4 calls")
+    # in-place one-shot runs the barrier between loads and stores each tile
+    G.note("in-place one-shot repeated")
+    for i in range(200):
+        work = [t.clone() for t in ins]
+        M.allreduce([t.data_ptr() for t in work], [t.data_ptr() for t in work], n, M.BFLOAT16, R,
+                    M.ALGO_ONE_SHOT, stream)
+    torch.cuda.synchronize()
+    G.assert_matches_oracle(work, want, "bf16", "in-place one-shot after repeats")
+
+
+def test_graph_capture_and_replay():
+    """Capture one call in a HIP graph and replay it; the semaphore epochs
+    live in device memory, so replays wait for the right counts."""
+    R, n = 8, 262_144
+    xs = P.rand_inputs(R, n, "bf16", seed=23)
+    want = O.allreduce(xs, "bf16")
+    ins = [G.to_device(x, "bf16") for x in xs]
+    G.channel(R)
+    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT):
+        outs = [G.poison_like(t) for t in ins]
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            # warm-up call outside the capture
+            M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, algo,
+                        s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, algo,
+                        torch.cuda.current_stream().cuda_stream)
+        for rep in range(20):
+            for o in outs:
+                o.zero_()  # eager work between replays (a fill kernel, not a memset node)
+            G.note(f"graph replay {rep} algo {algo}")
+            g.replay()
+            torch.cuda.synchronize()
+            G.assert_matches_oracle(outs, want, "bf16", f"graph replay {rep}")
+        for _ in range(80):
+            g.replay()
+        torch.cuda.synchronize()
+        G.assert_matches_oracle(outs, want, "bf16", "after 100 replays")
+        # eager calls still line up after the replays
+        outs2 = G.run(xs, "bf16", "two_shot", dev_inputs=ins)
+        G.assert_matches_oracle(outs2, want, "bf16", "eager after replays")
+        del g
+
+
+def test_timeout_is_reported_not_hung():
+    """Force a missing signal from the host (rank 1 skips signal()) with a
+    2 ms bound on every wait(): the kernel must exit, the status must read
+    TIMEOUT, further calls must refuse until reset, and a reset must bring
+    the channel back."""
+    R, n = 4, 100_000
+    xs = P.rand_inputs(R, n, "fp32", seed=31)
+    want = O.allreduce(xs, "fp32")
+    h = G.channel(R)
+    ins = [G.to_device(x, "fp32") for x in xs]
+    outs = [G.poison_like(t) for t in ins]
+    stream = torch.cuda.current_stream().cuda_stream
+    M.channel_set_fault_controls(h, wait_timeout_us=2000, drop_signal_rank=1)
+    try:
+        G.note("fault injection: rank 1 drops its signals, 2 ms wait bound")
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.FLOAT32, R, M.ALGO_TWO_SHOT,
+                    stream)
+        torch.cuda.synchronize()
+        assert M.channel_check(h) == M.ERR_TIMEOUT
+        st = M.raw_allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.FLOAT32, R,
+                             M.ALGO_TWO_SHOT, stream)
+        assert st == M.ERR_TIMEOUT
+    finally:
+        M.channel_set_fault_controls(h, 0, -1)
+        M.channel_reset(h)
+    assert M.channel_check(h) == M.SUCCESS
+    outs = G.run(xs, "fp32", "two_shot", dev_inputs=ins)
+    G.assert_matches_oracle(outs, want, "fp32", "after reset")
+
+
+def test_channel_registry():
+    dev = torch.cuda.current_device()
+    cached = G._channels.pop(11, None)  # drop the helper's own reference first
+    if cached is not None:
+        M.channel_destroy(cached)
+    a = M.channel_create(11, dev)
+    b = M.channel_create(11, dev)
+    assert a == b  # same (device, R): same set, refcounted
+    M.channel_destroy(b)
+    x = torch.zeros(64, device="cuda")
+    ins = [x.clone() for _ in range(11)]
+    outs = [x.clone() for _ in range(11)]
+    stream = torch.cuda.current_stream().cuda_stream
+    assert M.raw_allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], 64, M.FLOAT32, 11,
+                           M.ALGO_AUTO, stream) == M.SUCCESS
+    M.channel_destroy(a)
+    torch.cuda.synchronize()
+    assert M.raw_allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], 64, M.FLOAT32, 11,
+                           M.ALGO_AUTO, stream) == M.ERR_NOT_INITIALIZED
+    with pytest.raises(M.MsclError):
+        M.channel_destroy(a)
+
+
+def test_plan_geometry():
+    h = G.channel(8)
+    p = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_AUTO)
+    assert p.algo == M.ALGO_TWO_SHOT and p.uses_barrier == 1 and p.threads_per_workgroup == 256
+    assert p.chunk_elems == W.prefill_bf16().count // 8
+    assert 1 <= p.workgroups_per_rank
+    q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO)
+    assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 0
+    q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
+    assert q.uses_barrier == 1
+    r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert r16.chunk_elems % 8 == 0 and r16.chunk_elems * 16 >= W.ragged_outliers_bf16().count
