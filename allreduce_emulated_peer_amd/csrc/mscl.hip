@@ -52,11 +52,13 @@ namespace mscl {
 
 constexpr int kThreads = 256;
 
-// 16-byte vectors per thread per rank buffer per iteration: R*U loads in
-// flight per thread (16 for R >= 4) without running out of VGPRs.
+// 16-byte vectors per thread per rank buffer per tile.  With the software
+// pipelining of the two-shot, one vector per rank buffer (R loads in flight
+// per lane, 2R while the next tile is prefetched) measured fastest for R >= 5
+// on MI355X; small R keeps 8+ loads in flight with two or four.
 template <int R>
 constexpr int unroll_for() {
-  return R <= 4 ? 4 : (R <= 8 ? 2 : 1);
+  return R <= 2 ? 4 : (R <= 4 ? 2 : 1);
 }
 
 struct KernelArgs {
@@ -99,23 +101,28 @@ __device__ inline u32x4 reduce_partial(const KernelArgs& a, uint64_t vi, int nta
 // contiguous.  Full tiles (kFull) need no bounds checks, which keeps every
 // load of the tile issued back to back; the last, partial tile re-reads the
 // range's last vector in lanes past the end and skips their stores.
-template <int R, int U, bool kFull>
+template <int R, int U, bool kFull, bool kStream>
 __device__ inline void load_tile(u32x4 (&x)[U][R], const void* const* src, uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
     if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
 #pragma unroll
-    for (int p = 0; p < R; ++p) x[u][p] = load_vec(src[p], vi);
+    for (int p = 0; p < R; ++p) x[u][p] = kStream ? load_vec_nt(src[p], vi) : load_vec(src[p], vi);
   }
 }
 
-template <int U, bool kFull>
+template <int U, bool kFull, bool kStream>
 __device__ inline void store_tile(void* dst, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
-    if (kFull || vi < vend) store_vec(dst, vi, y[u]);
+    if (kFull || vi < vend) {
+      if (kStream)
+        store_vec_nt(dst, vi, y[u]);
+      else
+        store_vec(dst, vi, y[u]);
+    }
   }
 }
 
@@ -132,10 +139,10 @@ __device__ inline void oneshot_tile(const KernelArgs& a, const RankChannels& cha
                                     uint64_t vend) {
   u32x4 x[U][R];
   u32x4 y[U];
-  load_tile<R, U, kFull>(x, a.in, base, vend);
+  load_tile<R, U, kFull, false>(x, a.in, base, vend);  // every rank re-reads these: keep them cached
   reduce_tile<C, R, U>(y, x);
   if constexpr (kInPlace) chans.barrier_all();
-  store_tile<U, kFull>(dst, y, base, vend);
+  store_tile<U, kFull, false>(dst, y, base, vend);
 }
 
 template <class C, int R, bool kInPlace>
@@ -168,27 +175,27 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
   }
 }
 
-template <class C, int R, int U, bool kFull>
-__device__ inline void rs_tile(const KernelArgs& a, void* mine, uint64_t base, uint64_t vend) {
-  u32x4 x[U][R];
-  u32x4 y[U];
-  load_tile<R, U, kFull>(x, a.in, base, vend);  // get() from every peer
-  reduce_tile<C, R, U>(y, x);
-  store_tile<U, kFull>(mine, y, base, vend);
+// Cache policy of the two-shot: inputs are read exactly once and the peers'
+// outputs written exactly once, so both stream past the caches; the rank's
+// own reduced chunk is written and read back, so it stays cacheable.
+constexpr bool kStreamRsLoads = true;
+constexpr bool kStreamAgStores = true;
+
+template <int R, int U, bool kFull>
+__device__ inline void ag_store(const KernelArgs& a, int rank, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int p = 0; p < R; ++p)  // put() to every peer, written once
+    if (p != rank) store_tile<U, kFull, kStreamAgStores>(a.out[p], y, base, vend);
 }
 
-template <class C, int R, int U, bool kFull>
-__device__ inline void ag_tile(const KernelArgs& a, int rank, const void* mine, uint64_t base, uint64_t vend) {
-  u32x4 y[U];
+template <int U, bool kFull>
+__device__ inline void ag_load(u32x4 (&y)[U], const void* mine, uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
     if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
     y[u] = load_vec(mine, vi);
   }
-#pragma unroll
-  for (int p = 0; p < R; ++p)  // put() to every peer
-    if (p != rank) store_tile<U, kFull>(a.out[p], y, base, vend);
 }
 
 template <class C, int R>
@@ -198,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
   const int rank = blockIdx.x % R;
   const int slot = blockIdx.x / R;
+  const uint64_t B = a.nblk;
   const uint64_t n = a.count;
   const uint64_t lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, n);
   const uint64_t hi = std::min<uint64_t>(lo + a.chunk, n);
@@ -206,17 +214,46 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   // nonzero only for the non-empty chunk that holds the buffer's end
   const int ntail = hi > lo ? static_cast<int>(hi % V) : 0;
   const uint64_t nv = v_full - v_lo;
-  const uint64_t ntiles = (nv + kTile - 1) / kTile;
+  // Tiles t = slot, slot + B, ... belong to this slot.  Tiles below
+  // `nfull_tiles` lie wholly inside the chunk; at most one partial tile
+  // (index nfull_tiles) follows.
+  const uint64_t nfull_tiles = nv / kTile;
+  const bool owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(nfull_tiles % B);
   const RankChannels chans{a.ch, R, rank, slot};
   void* const mine = a.out[rank];
+  const uint64_t lane_base = v_lo + threadIdx.x;
 
-  // Reduce-scatter: chunk `rank` of every input -> own output.
-  for (uint64_t t = slot; t < ntiles; t += a.nblk) {
-    const uint64_t base = v_lo + t * kTile + threadIdx.x;
-    if ((t + 1) * kTile <= nv)
-      rs_tile<C, R, U, true>(a, mine, base, v_full);
-    else
-      rs_tile<C, R, U, false>(a, mine, base, v_full);
+  // Reduce-scatter: chunk `rank` of every input -> own output.  Software
+  // pipelined: the loads of the slot's next tile are issued before the
+  // current tile is reduced and stored, so each wave keeps R*U 16-byte
+  // loads in flight while it computes.
+  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+    uint64_t t = slot;
+    u32x4 cur[U][R];
+    load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * kTile, v_full);
+    while (true) {
+      const uint64_t tn = t + B;
+      const bool more = tn < nfull_tiles;
+      u32x4 nxt[U][R];
+      if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, v_full);
+      u32x4 y[U];
+      reduce_tile<C, R, U>(y, cur);
+      store_tile<U, true, false>(mine, y, lane_base + t * kTile, v_full);  // re-read by the all-gather: cached
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
+      t = tn;
+    }
+  }
+  if (owns_partial_tile) {
+    u32x4 x[U][R];
+    u32x4 y[U];
+    const uint64_t base = lane_base + nfull_tiles * kTile;
+    load_tile<R, U, false, kStreamRsLoads>(x, a.in, base, v_full);
+    reduce_tile<C, R, U>(y, x);
+    store_tile<U, false, false>(mine, y, base, v_full);
   }
   const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
   if (tail_owner) store_partial<C>(mine, v_full, reduce_partial<C, R>(a, v_full, ntail), ntail);
@@ -224,22 +261,35 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   // signal / wait with the same slot of every peer rank.
   chans.barrier_all();
 
-  // All-gather: put the reduced chunk into every peer's output, newest
-  // tiles first.  Same lanes, same vectors as the reduce-scatter.
-  if (ntiles > static_cast<uint64_t>(slot)) {
-    const uint64_t last = slot + (ntiles - 1 - slot) / a.nblk * a.nblk;
-    for (uint64_t t = last + a.nblk; t > static_cast<uint64_t>(slot);) {
-      t -= a.nblk;
-      const uint64_t base = v_lo + t * kTile + threadIdx.x;
-      if ((t + 1) * kTile <= nv)
-        ag_tile<C, R, U, true>(a, rank, mine, base, v_full);
-      else
-        ag_tile<C, R, U, false>(a, rank, mine, base, v_full);
-    }
-  }
+  // All-gather: put the reduced chunk into every peer's output, newest tiles
+  // first (they are the likeliest to still be in cache), again pipelined one
+  // tile ahead.  The same workgroup handles the same vectors as in the
+  // reduce-scatter, so in-place calls stay safe.
   if (tail_owner) {
     const u32x4 y = load_partial<C>(mine, v_full, ntail);
     put_to_peers<C, R>(a.out, rank, v_full, y, v_full, ntail);
+  }
+  if (owns_partial_tile) {
+    u32x4 y[U];
+    const uint64_t base = lane_base + nfull_tiles * kTile;
+    ag_load<U, false>(y, mine, base, v_full);
+    ag_store<R, U, false>(a, rank, y, base, v_full);
+  }
+  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+    uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
+    u32x4 cur[U];
+    ag_load<U, true>(cur, mine, lane_base + t * kTile, v_full);
+    while (true) {
+      const bool more = t >= static_cast<uint64_t>(slot) + B;
+      const uint64_t tn = more ? t - B : t;
+      u32x4 nxt[U];
+      if (more) ag_load<U, true>(nxt, mine, lane_base + tn * kTile, v_full);
+      ag_store<R, U, true>(a, rank, cur, lane_base + t * kTile, v_full);
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      t = tn;
+    }
   }
 }
 
@@ -274,7 +324,7 @@ KernelFn kernel_lookup(int kind, int dtype, int R) {
   return nullptr;
 }
 
-int unroll_for_runtime(int R) { return R <= 4 ? 4 : (R <= 8 ? 2 : 1); }
+int unroll_for_runtime(int R) { return R <= 2 ? 4 : (R <= 4 ? 2 : 1); }
 
 }  // namespace mscl
 
@@ -309,7 +359,7 @@ size_t env_size(const char* name, size_t dflt) {
 
 struct Config {
   size_t oneshot_max_bytes;  // selector threshold on bytes per rank buffer
-  size_t wg_target_total;    // default workgroups per launch (all ranks)
+  size_t wg_target_total;    // workgroups per launch, all ranks (0 = one per compute unit)
   size_t wg_per_rank;        // fixed workgroups per rank (0 = automatic)
   uint64_t wait_timeout_us;  // default bound of one device-side wait
 };
@@ -319,7 +369,7 @@ const Config& config() {
   static std::once_flag once;
   std::call_once(once, [] {
     c.oneshot_max_bytes = env_size("MSCL_ONESHOT_MAX_BYTES", 64 * 1024);
-    c.wg_target_total = env_size("MSCL_WG_TOTAL", 512);
+    c.wg_target_total = env_size("MSCL_WG_TOTAL", 0);
     c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
     c.wait_timeout_us = env_size("MSCL_WAIT_TIMEOUT_MS", 2000) * 1000;
   });
@@ -425,7 +475,10 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
     plan->uses_barrier = in_place ? 1 : 0;
   }
   uint64_t want = std::max<uint64_t>(1, (vectors + tile - 1) / tile);
-  uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, cfg.wg_target_total / R);
+  // One workgroup per compute unit in total measured best for the streaming
+  // phases (fewer concurrent streams keep HBM pages open longer).
+  const uint64_t total = cfg.wg_target_total ? cfg.wg_target_total : static_cast<uint64_t>(ch->cus);
+  uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, total / R);
   cap = std::min<uint64_t>(cap, ch->slots);  // every workgroup of a barrier must be resident
   plan->workgroups_per_rank = static_cast<int>(std::min(want, cap));
 }

@@ -76,6 +76,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--latency-iters", type=int, default=1000)
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the main workload (for profiler runs): no latency, decode or CPU legs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the R emulated ranks all live on one GPU, "
@@ -170,29 +172,32 @@ def main() -> int:
     log(f"[bench] {ms_per_step:.4f} ms/step wall, kernel mean {kern_ms.mean():.4f} ms (p50 {np.median(kern_ms):.4f}),"
         f" algbw {algbw:.1f} GB/s, {hbm_gbps:.1f} GB/s algorithmic HBM ({100 * hbm_gbps / HBM_PEAK_GBPS:.1f}% of peak)")
     traffic = committed_traffic()
-    roofline = {"bound": "hbm", "kernel": f"mscl_twoshot<BF16, 8>", "achieved": round(achieved, 1),
+    roofline = {"bound": "hbm", "kernel": "mscl_twoshot<BF16, 8>", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": alg_bytes,
-                "mean_launch_ms": round(float(kern_ms.mean()), 5)}
+                "traffic": None if traffic is None else int(traffic), "traffic_unit": "bytes per launch",
+                "traffic_gbps": None if traffic is None else round(traffic / (kern_ms.mean() / 1000.0) / 1e9, 1),
+                "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_ms": round(float(kern_ms.mean()), 5)}
     del ins, outs
     torch.cuda.empty_cache()
 
     # --------------------------------------------------- latency + decode
-    latency = {}
-    for lw in (W.sweep_bf16(14), W.integer_small()):
+    latency, decode = {}, None
+    for lw in (() if args.main_only else (W.sweep_bf16(14), W.integer_small())):
         li = device_inputs(lw)
         lo = [torch.empty_like(t) for t in li]
         p50, mean = p50_us(caller(lw, li, lo), args.latency_iters)
         latency[f"p50_us_16KiB_{lw.name}"] = round(p50, 2)
         log(f"[bench] {lw.name}: p50 {p50:.2f} us, mean {mean:.2f} us per call")
-    dw = W.decode_bf16()
-    di = device_inputs(dw)
-    do = [torch.empty_like(t) for t in di]
-    p50, mean = p50_us(caller(dw, di, do), args.latency_iters)
-    decode = {"workload": dw.name, "p50_us": round(p50, 2), "algbw_GBps_p50": round(dw.bytes_per_rank / p50 / 1e3, 1),
-              "cache": "hot (8 MiB footprint stays in cache)"}
-    log(f"[bench] {dw.name}: p50 {p50:.2f} us, algbw {decode['algbw_GBps_p50']} GB/s")
-    del di, do
+    if not args.main_only:
+        dw = W.decode_bf16()
+        di = device_inputs(dw)
+        do = [torch.empty_like(t) for t in di]
+        p50, mean = p50_us(caller(dw, di, do), args.latency_iters)
+        decode = {"workload": dw.name, "p50_us": round(p50, 2),
+                  "algbw_GBps_p50": round(dw.bytes_per_rank / p50 / 1e3, 1),
+                  "cache": "hot (8 MiB footprint stays in cache)"}
+        log(f"[bench] {dw.name}: p50 {p50:.2f} us, algbw {decode['algbw_GBps_p50']} GB/s")
+        del di, do
 
     if args.sweep:
         log("[bench] sweep R=8 bf16 (hot buffers): size, algo, p50 us, algbw GB/s, % HBM peak")
@@ -221,7 +226,7 @@ def main() -> int:
 
     # ---------------------------------------------------------- CPU oracle
     cpu = None
-    if not args.no_cpu_baseline:
+    if not (args.no_cpu_baseline or args.main_only):
         from oracle import cpu as C
 
         cores = min(os.cpu_count() or 1, 16)
