@@ -293,18 +293,94 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   }
 }
 
+// Two-shot with the all-gather put issued from registers: rank r reduces each
+// tile of chunk r and writes the rounded vector straight into every rank's
+// output (its own included), so the reduced chunk is never re-read and the
+// call moves exactly R*S bytes in and R*S out.  Inputs are read once and
+// outputs written once, so both stream past the caches.  The channel barrier
+// moves to the end, where it is the completion handshake of a put-based
+// exchange: signal() tells each peer "my puts into your output are done",
+// wait() collects the peers' signals for ours.  In place is safe without
+// ordering across ranks: the only reader of in[p][chunk r] is rank r, and
+// each lane loads a vector from every input before it stores that vector.
+template <class C, int R, int U, bool kFull>
+__device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int p = 0; p < R; ++p) store_tile<U, kFull, true>(a.out[p], y, base, vend);
+}
+
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
+  constexpr int V = C::V;
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t B = a.nblk;
+  const uint64_t n = a.count;
+  const uint64_t lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, n);
+  const uint64_t hi = std::min<uint64_t>(lo + a.chunk, n);
+  const uint64_t v_lo = lo / V;
+  const uint64_t v_full = hi / V;
+  const int ntail = hi > lo ? static_cast<int>(hi % V) : 0;
+  const uint64_t nv = v_full - v_lo;
+  const uint64_t nfull_tiles = nv / kTile;
+  const bool owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(nfull_tiles % B);
+  const RankChannels chans{a.ch, R, rank, slot};
+  const uint64_t lane_base = v_lo + threadIdx.x;
+
+  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+    uint64_t t = slot;
+    u32x4 cur[U][R];
+    load_tile<R, U, true, true>(cur, a.in, lane_base + t * kTile, v_full);
+    while (true) {
+      const uint64_t tn = t + B;
+      const bool more = tn < nfull_tiles;
+      u32x4 nxt[U][R];
+      if (more) load_tile<R, U, true, true>(nxt, a.in, lane_base + tn * kTile, v_full);
+      u32x4 y[U];
+      reduce_tile<C, R, U>(y, cur);
+      put_all_tile<C, R, U, true>(a, y, lane_base + t * kTile, v_full);
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
+      t = tn;
+    }
+  }
+  if (owns_partial_tile) {
+    u32x4 x[U][R];
+    u32x4 y[U];
+    const uint64_t base = lane_base + nfull_tiles * kTile;
+    load_tile<R, U, false, true>(x, a.in, base, v_full);
+    reduce_tile<C, R, U>(y, x);
+    put_all_tile<C, R, U, false>(a, y, base, v_full);
+  }
+  if (ntail != 0 && slot == 0 && threadIdx.x == 0) {
+    const u32x4 y = reduce_partial<C, R>(a, v_full, ntail);
+#pragma unroll
+    for (int p = 0; p < R; ++p) store_partial<C>(a.out[p], v_full, y, ntail);
+  }
+
+  // Completion: every put of this slot is done before its signal (release),
+  // and the peers' puts into this rank's output are visible after the wait.
+  chans.barrier_all();
+}
+
 // ----------------------------------------------------------------------------
 // Kernel tables
 // ----------------------------------------------------------------------------
 
 using KernelFn = void (*)(KernelArgs);
-enum { kAlgoOneShot = 0, kAlgoOneShotInPlace = 1, kAlgoTwoShot = 2, kNumKernelKinds = 3 };
+enum { kAlgoOneShot = 0, kAlgoOneShotInPlace = 1, kAlgoTwoShot = 2, kAlgoTwoShotFused = 3 };
 
 template <class C, int R>
 constexpr KernelFn kernel_for(int kind) {
-  return kind == kAlgoOneShot ? &mscl_oneshot<C, R, false>
+  return kind == kAlgoOneShot          ? &mscl_oneshot<C, R, false>
          : kind == kAlgoOneShotInPlace ? &mscl_oneshot<C, R, true>
-                                       : &mscl_twoshot<C, R>;
+         : kind == kAlgoTwoShot        ? &mscl_twoshot<C, R>
+                                       : &mscl_twoshot_fused<C, R>;
 }
 
 template <class C, int... Rs>
@@ -349,6 +425,11 @@ mscl_status_t fail_hip(hipError_t e, const char* what) {
 
 size_t elem_bytes(int dtype) { return dtype == MSCL_FLOAT32 ? 4 : 2; }
 
+bool valid_algo(int algo) {
+  return algo == MSCL_ALGO_AUTO || algo == MSCL_ALGO_ONE_SHOT || algo == MSCL_ALGO_TWO_SHOT ||
+         algo == MSCL_ALGO_TWO_SHOT_FUSED;
+}
+
 size_t env_size(const char* name, size_t dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
@@ -358,7 +439,7 @@ size_t env_size(const char* name, size_t dflt) {
 }
 
 struct Config {
-  size_t oneshot_max_bytes;  // selector threshold on bytes per rank buffer
+  size_t oneshot_max_bytes;  // selector threshold on bytes per rank buffer (SIZE_MAX = built-in table)
   size_t wg_target_total;    // workgroups per launch, all ranks (0 = one per compute unit)
   size_t wg_per_rank;        // fixed workgroups per rank (0 = automatic)
   uint64_t wait_timeout_us;  // default bound of one device-side wait
@@ -368,7 +449,7 @@ const Config& config() {
   static Config c;
   static std::once_flag once;
   std::call_once(once, [] {
-    c.oneshot_max_bytes = env_size("MSCL_ONESHOT_MAX_BYTES", 64 * 1024);
+    c.oneshot_max_bytes = env_size("MSCL_ONESHOT_MAX_BYTES", SIZE_MAX);  // SIZE_MAX: per-R table
     c.wg_target_total = env_size("MSCL_WG_TOTAL", 0);
     c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
     c.wait_timeout_us = env_size("MSCL_WAIT_TIMEOUT_MS", 2000) * 1000;
@@ -410,8 +491,7 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
     return fail(MSCL_ERR_INVALID_ARGUMENT, "nranks must be in 1..16");
   if (dtype != MSCL_FLOAT32 && dtype != MSCL_FLOAT16 && dtype != MSCL_BFLOAT16)
     return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
-  if (algo != MSCL_ALGO_AUTO && algo != MSCL_ALGO_ONE_SHOT && algo != MSCL_ALGO_TWO_SHOT)
-    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown algo");
+  if (!valid_algo(algo)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown algo");
   if (!inputs || !outputs) return fail(MSCL_ERR_INVALID_ARGUMENT, "inputs/outputs array is null");
   const size_t e = elem_bytes(dtype);
   if (count > SIZE_MAX / e) return fail(MSCL_ERR_INVALID_ARGUMENT, "count * element size overflows");
@@ -447,9 +527,23 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
   return MSCL_SUCCESS;
 }
 
-mscl_algo_t resolve_algo(size_t count, int dtype, int algo) {
+// Largest per-rank buffer for which AUTO picks the one-shot.  One-shot reads
+// R*S per rank (from cache while the buffers fit) against the two-shot's
+// S plus a barrier, so the crossover falls quickly with R.  Measured on
+// MI355X with bf16 buffers (p50 per call, one-shot vs two-shot): R = 2 up to
+// 16 MiB, R = 4 up to 2 MiB, R = 8 up to 256 KiB, R = 16 up to 128 KiB.
+size_t oneshot_max_bytes(int nranks) {
+  const size_t env = config().oneshot_max_bytes;
+  if (env != SIZE_MAX) return env;
+  if (nranks <= 2) return size_t(16) << 20;
+  if (nranks <= 4) return size_t(2) << 20;
+  if (nranks <= 8) return size_t(256) << 10;
+  return size_t(128) << 10;
+}
+
+mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo) {
   if (algo != MSCL_ALGO_AUTO) return static_cast<mscl_algo_t>(algo);
-  return count * elem_bytes(dtype) <= config().oneshot_max_bytes ? MSCL_ALGO_ONE_SHOT : MSCL_ALGO_TWO_SHOT;
+  return count * elem_bytes(dtype) <= oneshot_max_bytes(nranks) ? MSCL_ALGO_ONE_SHOT : MSCL_ALGO_TWO_SHOT;
 }
 
 void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t algo, bool in_place,
@@ -464,7 +558,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   plan->threads_per_workgroup = kThreads;
   plan->vectors_per_thread = unroll_for_runtime(R);
   uint64_t vectors;  // full vectors one rank covers
-  if (algo == MSCL_ALGO_TWO_SHOT) {
+  if (algo == MSCL_ALGO_TWO_SHOT || algo == MSCL_ALGO_TWO_SHOT_FUSED) {
     const uint64_t per = (count + R - 1) / R;
     const uint64_t c = (per + V - 1) / V * V;
     plan->chunk_elems = c;
@@ -511,7 +605,7 @@ mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, msc
   if (dtype != MSCL_FLOAT32 && dtype != MSCL_FLOAT16 && dtype != MSCL_BFLOAT16)
     return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (count > SIZE_MAX / elem_bytes(dtype)) return fail(MSCL_ERR_INVALID_ARGUMENT, "size overflows");
-  *out = resolve_algo(count, dtype, MSCL_ALGO_AUTO);
+  *out = resolve_algo(count, dtype, nranks, MSCL_ALGO_AUTO);
   return MSCL_SUCCESS;
 }
 
@@ -556,7 +650,7 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
   // workgroup that has not been scheduled.
   int min_resident = 1 << 30;
   for (int dt = 0; dt < 3; ++dt) {
-    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot}) {
+    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot, kAlgoTwoShotFused}) {
       int per_cu = 0;
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)),
                                                        kThreads, 0);
@@ -657,12 +751,11 @@ mscl_status_t mscl_channel_plan(mscl_channel_t ch, size_t count, mscl_dtype_t dt
   if (!plan) return fail(MSCL_ERR_INVALID_ARGUMENT, "plan is null");
   if (dtype != MSCL_FLOAT32 && dtype != MSCL_FLOAT16 && dtype != MSCL_BFLOAT16)
     return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
-  if (algo != MSCL_ALGO_AUTO && algo != MSCL_ALGO_ONE_SHOT && algo != MSCL_ALGO_TWO_SHOT)
-    return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown algo");
+  if (!valid_algo(algo)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown algo");
   if (count > SIZE_MAX / elem_bytes(dtype)) return fail(MSCL_ERR_INVALID_ARGUMENT, "size overflows");
   std::lock_guard<std::mutex> lock(g_mutex);
   if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
-  make_plan(ch, count, dtype, resolve_algo(count, dtype, algo), in_place != 0, plan);
+  make_plan(ch, count, dtype, resolve_algo(count, dtype, ch->nranks, algo), in_place != 0, plan);
   return MSCL_SUCCESS;
 }
 
@@ -690,7 +783,7 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
   if (__atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE) != MSCL_SUCCESS)
     return fail(MSCL_ERR_TIMEOUT, "an earlier call timed out; call mscl_channel_reset");
 
-  const mscl_algo_t resolved = resolve_algo(count, dtype, algo);
+  const mscl_algo_t resolved = resolve_algo(count, dtype, nranks, algo);
   mscl_plan_t plan;
   make_plan(ch, count, dtype, resolved, in_place, &plan);
 
@@ -710,7 +803,10 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
   a.ch.drop_rank = drop_rank;
   a.ch.timeout_ticks = timeout_us * ch->wall_clock_khz / 1000;
 
-  int kind = resolved == MSCL_ALGO_TWO_SHOT ? kAlgoTwoShot : (in_place ? kAlgoOneShotInPlace : kAlgoOneShot);
+  const int kind = resolved == MSCL_ALGO_TWO_SHOT         ? kAlgoTwoShot
+                   : resolved == MSCL_ALGO_TWO_SHOT_FUSED ? kAlgoTwoShotFused
+                   : in_place                             ? kAlgoOneShotInPlace
+                                                          : kAlgoOneShot;
   KernelFn fn = kernel_lookup(kind, dtype, nranks);
   if (!fn) return fail(MSCL_ERR_INVALID_ARGUMENT, "no kernel for this dtype and rank count");
   const dim3 grid(static_cast<unsigned>(nranks * plan.workgroups_per_rank));

@@ -54,9 +54,12 @@ typedef enum {
 } mscl_dtype_t;
 
 typedef enum {
-  MSCL_ALGO_AUTO = 0,     /* one-shot up to a size threshold, two-shot above it */
-  MSCL_ALGO_ONE_SHOT = 1, /* every rank reads all R inputs and writes its own output */
-  MSCL_ALGO_TWO_SHOT = 2  /* reduce-scatter, device barrier, all-gather put */
+  MSCL_ALGO_AUTO = 0,          /* one-shot up to a size threshold, two-shot above it */
+  MSCL_ALGO_ONE_SHOT = 1,      /* every rank reads all R inputs and writes its own output */
+  MSCL_ALGO_TWO_SHOT = 2,      /* reduce-scatter, device signal/wait barrier, all-gather put */
+  MSCL_ALGO_TWO_SHOT_FUSED = 3 /* reduce-scatter whose all-gather put goes out from registers,
+                                  then a completion signal/wait barrier (no re-read of the
+                                  reduced chunk) */
 } mscl_algo_t;
 
 typedef int mscl_status_t;
@@ -147,8 +150,8 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  *   dtype   : element type of inputs and outputs.
  *   nranks  : R, 1..MSCL_MAX_RANKS; a channel set for (current device, R)
  *             must exist (mscl_channel_create).
- *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT or _TWO_SHOT.  All give bit-identical
- *             results.
+ *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT, _TWO_SHOT or _TWO_SHOT_FUSED.  All
+ *             give bit-identical results.
  *   stream  : hipStream_t on the current device (NULL = default stream).
  * Every pointer must be 16-byte aligned and on the current device.  The call
  * is asynchronous: it validates, launches one kernel on `stream` and
@@ -164,9 +167,11 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
 
 /*
  * The algorithm MSCL_ALGO_AUTO resolves to for this size: one-shot when the
- * per-rank buffer (count * element size) is at most the one-shot threshold,
- * else two-shot.  Pure host computation.  The threshold can be overridden
- * with the environment variable MSCL_ONESHOT_MAX_BYTES (read once).
+ * per-rank buffer (count * element size) is at most a threshold that falls
+ * with R (measured crossovers on MI355X: 16 MiB for R <= 2, 2 MiB for
+ * R <= 4, 256 KiB for R <= 8, 128 KiB above), else two-shot.  Pure host
+ * computation.  The environment variable MSCL_ONESHOT_MAX_BYTES (read once)
+ * replaces the table with one threshold for every R.
  * Errors: INVALID_ARGUMENT.
  */
 mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, mscl_algo_t* out);

@@ -63,7 +63,8 @@ def test_bad_nranks(R):
 def test_bad_dtype_and_algo():
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 3, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, -1, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
-    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 3, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 4, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, -1, 0) == M.ERR_INVALID_ARGUMENT
 
 
 def test_null_arrays_and_pointers():
@@ -112,12 +113,18 @@ def test_size_overflow():
 
 
 def test_selector():
-    # one-shot up to the threshold (64 KiB per rank buffer by default), two-shot above
-    assert M.select_algo(1, M.BFLOAT16, 8) == M.ALGO_ONE_SHOT
-    assert M.select_algo(32 * 1024, M.BFLOAT16, 8) == M.ALGO_ONE_SHOT
-    assert M.select_algo(32 * 1024 + 1, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
-    assert M.select_algo(16 * 1024, M.FLOAT32, 4) == M.ALGO_ONE_SHOT
-    assert M.select_algo(64 * 1024 * 1024, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
+    # one-shot up to a threshold that falls with R, two-shot above
+    KiB, MiB = 1024, 1024 * 1024
+    for R, limit in ((1, 16 * MiB), (2, 16 * MiB), (3, 2 * MiB), (4, 2 * MiB), (5, 256 * KiB), (8, 256 * KiB),
+                     (9, 128 * KiB), (16, 128 * KiB)):
+        assert M.select_algo(1, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
+        assert M.select_algo(limit // 2, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
+        assert M.select_algo(limit // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
+        assert M.select_algo(limit // 4, M.FLOAT32, R) == M.ALGO_ONE_SHOT
+        assert M.select_algo(limit // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT
+    assert M.select_algo(4096, M.FLOAT32, 4) == M.ALGO_ONE_SHOT  # the 16 KiB integer workload
+    assert M.select_algo(32 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT  # 512 KiB decode shape
+    assert M.select_algo(64 * MiB, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
     with pytest.raises(M.MsclError):
         M.select_algo(10, 7, 8)
     with pytest.raises(M.MsclError):

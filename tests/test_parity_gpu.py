@@ -29,7 +29,7 @@ def gpu():
     yield
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "auto"])
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "auto"])
 def test_integer_workload_exact(algo):
     w = W.integer_small()
     xs = W.generate_all(w)
@@ -41,7 +41,7 @@ def test_integer_workload_exact(algo):
     G.assert_matches_oracle(outs, O.allreduce(xs, "fp32"), "fp32", w.name)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "auto"])
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "auto"])
 def test_decode_bf16(algo):
     w = W.decode_bf16()
     xs = W.generate_all(w)
@@ -68,7 +68,7 @@ def test_tiny_brute_force(dtype):
                 b[m] = g.choice(specials, size=int(m.sum()))
             xs = [P.from_bits(b, dtype) for b in bitsx]
             want = O.allreduce(xs, dtype)
-            for algo in ("one_shot", "two_shot"):
+            for algo in G.EXPLICIT:
                 for in_place in (False, True):
                     G.note(f"tiny {dtype} R={R} n={n} {algo} in_place={in_place}")
                     outs = G.run(xs, dtype, algo, in_place=in_place)
@@ -80,7 +80,7 @@ def test_hand_cases_on_gpu():
     Inf/NaN, overflow, subnormals) through both kernels."""
     for dtype, ins, want in P.load_hand_cases():
         xs = [P.from_bits(np.array([v] * 37), dtype) for v in ins]  # 37: full vectors + a tail
-        for algo in ("one_shot", "two_shot"):
+        for algo in G.EXPLICIT:
             G.note(f"hand case {dtype} {[hex(v) for v in ins]} {algo}")
             outs = G.run(xs, dtype, algo)
             got = G.to_host_bits(outs[0], dtype)
@@ -91,7 +91,7 @@ def test_hand_cases_on_gpu():
                 assert np.all(got == int(want, 16)), f"{dtype} {ins} {algo}: {hex(int(got[0]))} != {want}"
 
 
-@pytest.mark.parametrize("algo", ["auto", "one_shot"])
+@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused"])
 def test_prefill_bf16_full(algo):
     w = W.prefill_bf16()
     xs = W.generate_all(w)
@@ -101,7 +101,7 @@ def test_prefill_bf16_full(algo):
     G.assert_matches_oracle_on_device(outs, want, "bf16", w.name)
 
 
-@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot"])
+@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused"])
 def test_ragged_outliers_full(algo):
     w = W.ragged_outliers_bf16()
     xs = W.generate_all(w)
@@ -114,16 +114,16 @@ def test_ragged_outliers_full(algo):
 
 
 def test_fp16_sweep():
-    """1 KiB .. 256 MiB per buffer, R = 8, both algorithms.  Up to 16 MiB the
+    """1 KiB .. 256 MiB per buffer, R = 8, every algorithm.  Up to 16 MiB the
     whole result is compared with the oracle; above, 64 Ki sampled elements
-    (plus both ends) are, and the two algorithms must agree bit for bit on
-    every element."""
+    (plus both ends) are, and the algorithms must agree bit for bit on every
+    element."""
     for k in range(10, 29):
         w = W.sweep_fp16(k)
         xs = W.generate_all(w)
         dev_in = [G.to_device(x, "fp16") for x in xs]
         res = {}
-        for algo in ("one_shot", "two_shot"):
+        for algo in G.EXPLICIT:
             G.note(f"{w.name} {algo}")
             res[algo] = G.run(xs, "fp16", algo, dev_inputs=dev_in)
         if k <= 24:
@@ -138,12 +138,13 @@ def test_fp16_sweep():
                 got = G.to_host_bits(outs[0], "fp16")[idx]
                 assert np.array_equal(got, want.view(np.uint16)), f"{w.name} {algo}: sampled mismatch"
             for r in range(8):
-                assert torch.equal(res["one_shot"][r].view(torch.uint8), res["two_shot"][r].view(torch.uint8))
+                for algo in ("two_shot", "two_shot_fused"):
+                    assert torch.equal(res["one_shot"][r].view(torch.uint8), res[algo][r].view(torch.uint8))
         del dev_in, res
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "two_shot"])
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused"])
 @pytest.mark.parametrize("R,n,dtype", [(8, 3 * 256 * 2 * 8 * 64 + 5, "bf16"), (16, 1_000_003, "bf16"),
                                        (4, 777_777, "fp32"), (3, 1 << 20, "fp16"), (8, 9_437_185, "fp16")])
 def test_in_place(algo, R, n, dtype):
@@ -158,7 +159,7 @@ def test_mixed_in_place_and_out_of_place():
     R, n = 6, 123_457
     xs = P.rand_inputs(R, n, "bf16", seed=5)
     want = O.allreduce(xs, "bf16")
-    for algo in ("one_shot", "two_shot"):
+    for algo in G.EXPLICIT:
         ins = [G.to_device(x, "bf16") for x in xs]
         outs = [ins[r] if r % 2 == 0 else G.poison_like(ins[r]) for r in range(R)]
         G.channel(R)
@@ -174,7 +175,7 @@ def test_non_default_stream():
     xs = W.generate_all(w)
     want = O.allreduce(xs, "bf16")
     s = torch.cuda.Stream()
-    for algo in ("one_shot", "two_shot"):
+    for algo in G.EXPLICIT:
         G.note(f"side stream {algo}")
         outs = G.run(xs, "bf16", algo, stream=s)
         G.assert_matches_oracle(outs, want, "bf16", f"side stream {algo}")
@@ -190,9 +191,9 @@ def test_repeated_calls_keep_epochs():
     outs = [G.poison_like(t) for t in ins]
     h = G.channel(R)
     stream = torch.cuda.current_stream().cuda_stream
-    G.note("10^4 repeated two-shot / in-place one-shot calls")
+    G.note("10^4 repeated one-shot / two-shot / fused two-shot calls")
     for i in range(10_000):
-        algo = M.ALGO_TWO_SHOT if i % 3 else M.ALGO_ONE_SHOT
+        algo = (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED)[i % 3]
         M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, algo, stream)
         if i % 1000 == 999:
             torch.cuda.synchronize()
@@ -218,7 +219,7 @@ def test_graph_capture_and_replay():
     want = O.allreduce(xs, "bf16")
     ins = [G.to_device(x, "bf16") for x in xs]
     G.channel(R)
-    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT):
+    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_FUSED):
         outs = [G.poison_like(t) for t in ins]
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -249,7 +250,8 @@ def test_graph_capture_and_replay():
         del g
 
 
-def test_timeout_is_reported_not_hung():
+@pytest.mark.parametrize("algo", [M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED])
+def test_timeout_is_reported_not_hung(algo):
     """Force a missing signal from the host (rank 1 skips signal()) with a
     2 ms bound on every wait(): the kernel must exit, the status must read
     TIMEOUT, further calls must refuse until reset, and a reset must bring
@@ -264,18 +266,18 @@ def test_timeout_is_reported_not_hung():
     M.channel_set_fault_controls(h, wait_timeout_us=2000, drop_signal_rank=1)
     try:
         G.note("fault injection: rank 1 drops its signals, 2 ms wait bound")
-        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.FLOAT32, R, M.ALGO_TWO_SHOT,
-                    stream)
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.FLOAT32, R, algo, stream)
         torch.cuda.synchronize()
         assert M.channel_check(h) == M.ERR_TIMEOUT
         st = M.raw_allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.FLOAT32, R,
-                             M.ALGO_TWO_SHOT, stream)
+                             algo, stream)
         assert st == M.ERR_TIMEOUT
     finally:
         M.channel_set_fault_controls(h, 0, -1)
         M.channel_reset(h)
     assert M.channel_check(h) == M.SUCCESS
-    outs = G.run(xs, "fp32", "two_shot", dev_inputs=ins)
+    outs = G.run(xs, "fp32", {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_TWO_SHOT_FUSED: "two_shot_fused"}[algo],
+                 dev_inputs=ins)
     G.assert_matches_oracle(outs, want, "fp32", "after reset")
 
 
