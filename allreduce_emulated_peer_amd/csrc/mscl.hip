@@ -8,9 +8,11 @@
 // ("PortChannel and MemoryChannel").  This file holds the two kernels and the
 // host side of the C ABI declared in include/mscl.h.
 //
-// Rank layout.  Workgroup w of a launch is emulated rank (w % R), channel
-// slot (w / R); with the hardware's round-robin dispatch of workgroups over
-// the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.  Each
+// Rank layout.  In the two-shot, workgroup w of a launch is emulated rank
+// (w % R), channel slot (w / R); with the hardware's round-robin dispatch of
+// workgroups over the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.
+// The one-shot groups instead the R ranks of a slot on one XCD, because there
+// every rank re-reads the same input lines.  Each
 // workgroup has 256 threads (4 wavefronts of 64); each thread keeps U
 // 16-byte vectors of each of the R rank buffers in flight per iteration.
 //
@@ -52,6 +54,11 @@ namespace mscl {
 
 constexpr int kThreads = 256;
 
+// gfx950 parts (MI350 series) have 8 accelerator complex dies (XCDs), each
+// with its own L2; the dispatcher deals workgroups to them round-robin, so
+// workgroup w runs on XCD w % 8.
+constexpr int kXcds = 8;
+
 // 16-byte vectors per thread per rank buffer per tile.  With the software
 // pipelining of the two-shot, one vector per rank buffer (R loads in flight
 // per lane, 2R while the next tile is prefetched) measured fastest for R >= 5
@@ -67,6 +74,7 @@ struct KernelArgs {
   uint64_t count;  // elements per rank buffer
   uint64_t chunk;  // two-shot: elements per rank chunk, a multiple of V
   uint32_t nblk;   // workgroups (slots) per rank in this launch
+  uint32_t xcd_grouped;  // one-shot: all ranks of a slot on one XCD (needs nblk % 8 == 0)
   ChannelArgs ch;
 };
 
@@ -150,8 +158,12 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
   constexpr int V = C::V;
   constexpr int U = unroll_for<R>();
   constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
-  const int rank = blockIdx.x % R;
-  const int slot = blockIdx.x / R;
+  // Every rank reads the same tile of all R inputs.  Putting the R ranks'
+  // workgroups of one slot on the same XCD lets that XCD's L2 serve the R-fold
+  // re-reads of each line (measured: R = 8 at 1 MiB per rank, 12.2 -> 6.6 us).
+  const int w = blockIdx.x;
+  const int rank = a.xcd_grouped ? (w / kXcds) % R : w % R;
+  const int slot = a.xcd_grouped ? (w / kXcds / R) * kXcds + w % kXcds : w / R;
   const uint64_t n = a.count;
   const uint64_t nfull = n / V;
   const int ntail = static_cast<int>(n % V);
@@ -530,15 +542,16 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
 // Largest per-rank buffer for which AUTO picks the one-shot.  One-shot reads
 // R*S per rank (from cache while the buffers fit) against the two-shot's
 // S plus a barrier, so the crossover falls quickly with R.  Measured on
-// MI355X with bf16 buffers (p50 per call, one-shot vs two-shot): R = 2 up to
-// 16 MiB, R = 4 up to 2 MiB, R = 8 up to 256 KiB, R = 16 up to 128 KiB.
+// MI355X with bf16 buffers (device time per call, calls replayed from a
+// graph, one-shot with XCD-grouped ranks): one-shot is fastest up to 32 MiB
+// at R = 2, 8 MiB at R = 4, 2 MiB at R = 8 and 256 KiB at R = 16.
 size_t oneshot_max_bytes(int nranks) {
   const size_t env = config().oneshot_max_bytes;
   if (env != SIZE_MAX) return env;
-  if (nranks <= 2) return size_t(16) << 20;
-  if (nranks <= 4) return size_t(2) << 20;
-  if (nranks <= 8) return size_t(256) << 10;
-  return size_t(128) << 10;
+  if (nranks <= 2) return size_t(32) << 20;
+  if (nranks <= 4) return size_t(8) << 20;
+  if (nranks <= 8) return size_t(2) << 20;
+  return size_t(256) << 10;
 }
 
 mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo) {
@@ -574,7 +587,10 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   const uint64_t total = cfg.wg_target_total ? cfg.wg_target_total : static_cast<uint64_t>(ch->cus);
   uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, total / R);
   cap = std::min<uint64_t>(cap, ch->slots);  // every workgroup of a barrier must be resident
-  plan->workgroups_per_rank = static_cast<int>(std::min(want, cap));
+  uint64_t b = std::min(want, cap);
+  if (algo == MSCL_ALGO_ONE_SHOT && cap >= kXcds)
+    b = std::min((b + kXcds - 1) / kXcds * kXcds, cap / kXcds * kXcds);  // whole XCD groups
+  plan->workgroups_per_rank = static_cast<int>(b);
 }
 
 }  // namespace
@@ -796,6 +812,7 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
   a.count = count;
   a.chunk = plan.chunk_elems;
   a.nblk = static_cast<uint32_t>(plan.workgroups_per_rank);
+  a.xcd_grouped = (resolved == MSCL_ALGO_ONE_SHOT && a.nblk % kXcds == 0) ? 1u : 0u;
   a.ch.inbound = ch->inbound;
   a.ch.consumed = ch->consumed;
   a.ch.status = ch->status_dev;
