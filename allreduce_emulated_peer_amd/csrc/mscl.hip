@@ -149,7 +149,9 @@ __device__ inline void oneshot_tile(const KernelArgs& a, const RankChannels& cha
   u32x4 y[U];
   load_tile<R, U, kFull, false>(x, a.in, base, vend);  // every rank re-reads these: keep them cached
   reduce_tile<C, R, U>(y, x);
-  if constexpr (kInPlace) chans.barrier_all();
+  // Peers read this rank's input until they signal; their loads must be
+  // complete before this rank overwrites it (write after read across ranks).
+  if constexpr (kInPlace) chans.template barrier_all<true>();
   store_tile<U, kFull, false>(dst, y, base, vend);
 }
 
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
   if (ntail != 0 && slot == 0) {
     u32x4 y = {0u, 0u, 0u, 0u};
     if (threadIdx.x == 0) y = reduce_partial<C, R>(a, nfull, ntail);
-    if constexpr (kInPlace) chans.barrier_all();
+    if constexpr (kInPlace) chans.template barrier_all<true>();
     if (threadIdx.x == 0) store_partial<C>(dst, nfull, y, ntail);
   }
 }
@@ -270,8 +272,14 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
   if (tail_owner) store_partial<C>(mine, v_full, reduce_partial<C, R>(a, v_full, ntail), ntail);
 
-  // signal / wait with the same slot of every peer rank.
-  chans.barrier_all();
+  // signal / wait with the same slot of every peer rank.  Arrival only: no
+  // data crosses ranks here.  The all-gather below reads only vectors this
+  // lane itself wrote above (program order), and writes peer locations that
+  // no peer reads during this call (rank p reads only its own chunk of every
+  // input, and in place rank r alone reads in[p][chunk r], earlier, in this
+  // lane).  Publishing or acquiring memory here would only cost an L2
+  // write-back and invalidate per workgroup.
+  chans.template barrier_all<false>();
 
   // All-gather: put the reduced chunk into every peer's output, newest tiles
   // first (they are the likeliest to still be in cache), again pipelined one
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
 
   // Completion: every put of this slot is done before its signal (release),
   // and the peers' puts into this rank's output are visible after the wait.
-  chans.barrier_all();
+  chans.template barrier_all<true>();
 }
 
 // ----------------------------------------------------------------------------
@@ -543,15 +551,17 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
 // R*S per rank (from cache while the buffers fit) against the two-shot's
 // S plus a barrier, so the crossover falls quickly with R.  Measured on
 // MI355X with bf16 buffers (device time per call, calls replayed from a
-// graph, one-shot with XCD-grouped ranks): one-shot is fastest up to 32 MiB
-// at R = 2, 8 MiB at R = 4, 2 MiB at R = 8 and 256 KiB at R = 16.
+// graph, one-shot with XCD-grouped ranks, two-shot with the arrival-only
+// barrier): at R = 2 the one-shot wins at every size (64 MiB per rank: 41 us
+// against 50 us); otherwise it wins up to 2 MiB at R = 4, 512 KiB at R = 8
+// and 128 KiB at R = 16.
 size_t oneshot_max_bytes(int nranks) {
   const size_t env = config().oneshot_max_bytes;
   if (env != SIZE_MAX) return env;
-  if (nranks <= 2) return size_t(32) << 20;
-  if (nranks <= 4) return size_t(8) << 20;
-  if (nranks <= 8) return size_t(2) << 20;
-  return size_t(256) << 10;
+  if (nranks <= 2) return SIZE_MAX;
+  if (nranks <= 4) return size_t(2) << 20;
+  if (nranks <= 8) return size_t(512) << 10;
+  return size_t(128) << 10;
 }
 
 mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo) {

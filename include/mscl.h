@@ -168,8 +168,8 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
 /*
  * The algorithm MSCL_ALGO_AUTO resolves to for this size: one-shot when the
  * per-rank buffer (count * element size) is at most a threshold that falls
- * with R (measured crossovers on MI355X: 32 MiB for R <= 2, 8 MiB for
- * R <= 4, 2 MiB for R <= 8, 256 KiB above), else two-shot.  Pure host
+ * with R (measured crossovers on MI355X: no limit for R <= 2, 2 MiB for
+ * R <= 4, 512 KiB for R <= 8, 128 KiB above), else two-shot.  Pure host
  * computation.  The environment variable MSCL_ONESHOT_MAX_BYTES (read once)
  * replaces the table with one threshold for every R.
  * Errors: INVALID_ARGUMENT.

@@ -115,16 +115,17 @@ def test_size_overflow():
 def test_selector():
     # one-shot up to a threshold that falls with R, two-shot above
     KiB, MiB = 1024, 1024 * 1024
-    for R, limit in ((1, 32 * MiB), (2, 32 * MiB), (3, 8 * MiB), (4, 8 * MiB), (5, 2 * MiB), (8, 2 * MiB),
-                     (9, 256 * KiB), (16, 256 * KiB)):
+    for R, limit in ((3, 2 * MiB), (4, 2 * MiB), (5, 512 * KiB), (8, 512 * KiB), (9, 128 * KiB), (16, 128 * KiB)):
         assert M.select_algo(1, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
         assert M.select_algo(limit // 4, M.FLOAT32, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT
+    for R in (1, 2):  # one-shot at every size
+        assert M.select_algo(2 ** 40, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
     assert M.select_algo(4096, M.FLOAT32, 4) == M.ALGO_ONE_SHOT  # the 16 KiB integer workload
     assert M.select_algo(32 * 8192, M.BFLOAT16, 8) == M.ALGO_ONE_SHOT  # 512 KiB decode shape
-    assert M.select_algo(1024 * 1024 + 1, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
+    assert M.select_algo(32 * 8192 + 1, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
     assert M.select_algo(64 * MiB, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
     with pytest.raises(M.MsclError):
         M.select_algo(10, 7, 8)
