@@ -29,6 +29,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 struct F32 {
   static constexpr int kElemBytes = 4;
   static constexpr int V = 4;
+  using Bits = uint32_t;
+  __device__ static inline float widen(Bits b) { return __builtin_bit_cast(float, b); }
+  __device__ static inline Bits narrow(float f) { return __builtin_bit_cast(uint32_t, f); }
   __device__ static inline void unpack(const u32x4& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -50,6 +53,9 @@ struct F32 {
 struct BF16 {
   static constexpr int kElemBytes = 2;
   static constexpr int V = 8;
+  using Bits = uint16_t;
+  __device__ static inline float widen(Bits b) { return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16); }
+  __device__ static inline Bits narrow(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
   __device__ static inline void unpack(const u32x4& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -72,6 +78,9 @@ struct BF16 {
 struct F16 {
   static constexpr int kElemBytes = 2;
   static constexpr int V = 8;
+  using Bits = uint16_t;
+  __device__ static inline float widen(Bits b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
+  __device__ static inline Bits narrow(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
   __device__ static inline void unpack(const u32x4& v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

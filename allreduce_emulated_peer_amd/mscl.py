@@ -39,7 +39,8 @@ ALGO_CODES = {"auto": ALGO_AUTO, "one_shot": ALGO_ONE_SHOT, "two_shot": ALGO_TWO
 EXPORTS = (
     "mscl_version", "mscl_status_string", "mscl_last_error_string", "mscl_channel_create",
     "mscl_channel_destroy", "mscl_channel_check", "mscl_channel_reset", "mscl_allreduce",
-    "mscl_select_algo", "mscl_channel_plan", "mscl_channel_set_fault_controls",
+    "mscl_select_algo", "mscl_channel_plan", "mscl_channel_set_fault_controls", "mscl_reduce_scatter",
+    "mscl_allgather",
 )
 
 
@@ -86,6 +87,9 @@ def load(path: str = LIB_PATH):
         getattr(lib, name).argtypes = [vp]
     lib.mscl_allreduce.restype = c_int
     lib.mscl_allreduce.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, c_int, vp]
+    for name in ("mscl_reduce_scatter", "mscl_allgather"):
+        getattr(lib, name).restype = c_int
+        getattr(lib, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, vp]
     lib.mscl_select_algo.restype = c_int
     lib.mscl_select_algo.argtypes = [c_size, c_int, c_int, ctypes.POINTER(c_int)]
     lib.mscl_channel_plan.restype = c_int
@@ -129,6 +133,28 @@ def raw_allreduce(inputs, outputs, count: int, dtype: int, nranks: int, algo: in
 def allreduce(inputs, outputs, count: int, dtype: int, nranks: int, algo: int = ALGO_AUTO, stream: int = 0) -> None:
     """mscl_allreduce: `inputs` / `outputs` are sequences of device addresses."""
     _check(raw_allreduce(inputs, outputs, count, dtype, nranks, algo, stream), "mscl_allreduce")
+
+
+def raw_reduce_scatter(inputs, outputs, recvcount: int, dtype: int, nranks: int, stream: int) -> int:
+    ins = _ptr_array(inputs) if inputs is not None else None
+    outs = _ptr_array(outputs) if outputs is not None else None
+    return load().mscl_reduce_scatter(ins, outs, recvcount, dtype, nranks, ctypes.c_void_p(int(stream) or None))
+
+
+def reduce_scatter(inputs, outputs, recvcount: int, dtype: int, nranks: int, stream: int = 0) -> None:
+    """mscl_reduce_scatter: inputs hold nranks*recvcount elements, outputs recvcount."""
+    _check(raw_reduce_scatter(inputs, outputs, recvcount, dtype, nranks, stream), "mscl_reduce_scatter")
+
+
+def raw_allgather(inputs, outputs, sendcount: int, dtype: int, nranks: int, stream: int) -> int:
+    ins = _ptr_array(inputs) if inputs is not None else None
+    outs = _ptr_array(outputs) if outputs is not None else None
+    return load().mscl_allgather(ins, outs, sendcount, dtype, nranks, ctypes.c_void_p(int(stream) or None))
+
+
+def allgather(inputs, outputs, sendcount: int, dtype: int, nranks: int, stream: int = 0) -> None:
+    """mscl_allgather: inputs hold sendcount elements, outputs nranks*sendcount."""
+    _check(raw_allgather(inputs, outputs, sendcount, dtype, nranks, stream), "mscl_allgather")
 
 
 def channel_create(nranks: int, device: int) -> int:

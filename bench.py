@@ -234,6 +234,57 @@ def main() -> int:
         log(f"[bench] {dw.name}: p50 {p50:.2f} us, graph {dev_us:.2f} us/call, algbw {decode['algbw_GBps_graph']} GB/s")
         del di, do
 
+    collectives = None
+    if not args.main_only:
+        # ReduceScatter of the prefill buffers (16 MiB blocks) and AllGather of
+        # the blocks back; algorithmic bytes: everything read once + written once
+        import ctypes
+        R, rc = w.nranks, w.count // w.nranks
+        ci = device_inputs(w)
+        blocks = [torch.empty(rc, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        gathered = [torch.empty(w.count, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        lib = M.load()
+        rs_in = (ctypes.c_void_p * R)(*[t.data_ptr() for t in ci])
+        rs_out = (ctypes.c_void_p * R)(*[t.data_ptr() for t in blocks])
+        ag_out = (ctypes.c_void_p * R)(*[t.data_ptr() for t in gathered])
+
+        def timed(fn, reps=5):
+            g = torch.cuda.CUDAGraph()
+            fn(stream.cuda_stream)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn(torch.cuda.current_stream().cuda_stream)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1000.0 / reps
+
+        def rs(s):
+            assert lib.mscl_reduce_scatter(rs_in, rs_out, rc, M.BFLOAT16, R, ctypes.c_void_p(s)) == M.SUCCESS
+
+        def ag(s):
+            assert lib.mscl_allgather(rs_out, ag_out, rc, M.BFLOAT16, R, ctypes.c_void_p(s)) == M.SUCCESS
+        t_rs, t_ag = timed(rs), timed(ag)
+        b_rs = R * S + R * rc * 2  # R inputs of S read, R blocks written
+        b_ag = R * rc * 2 + R * S  # R blocks read, R outputs of S written
+        collectives = {
+            "reduce_scatter": {"shape": f"R=8 bf16, {S} B inputs, {rc * 2} B blocks", "us": round(t_rs, 1),
+                               "GBps": round(b_rs / t_rs / 1e3, 1),
+                               "pct_hbm_peak": round(100 * b_rs / t_rs / 1e3 / HBM_PEAK_GBPS, 1)},
+            "allgather": {"shape": f"R=8 bf16, {rc * 2} B blocks, {S} B outputs", "us": round(t_ag, 1),
+                          "GBps": round(b_ag / t_ag / 1e3, 1),
+                          "pct_hbm_peak": round(100 * b_ag / t_ag / 1e3 / HBM_PEAK_GBPS, 1)},
+            "note": "device time per call, graph replay; bytes = data read once + written once"}
+        log(f"[bench] reduce_scatter {t_rs:.1f} us ({collectives['reduce_scatter']['GBps']} GB/s), "
+            f"allgather {t_ag:.1f} us ({collectives['allgather']['GBps']} GB/s)")
+        del ci, blocks, gathered
+        torch.cuda.empty_cache()
+
     if args.sweep:
         log("[bench] sweep R=8 bf16 (hot buffers, graph-replayed device time): bytes/rank, us one/two/fused, "
             "best algbw GB/s, % HBM peak")
@@ -296,6 +347,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "latency": latency,
         "decode_512KiB": decode,
+        "collectives": collectives,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -166,6 +166,51 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
                              mscl_dtype_t dtype, int nranks, mscl_algo_t algo, void* stream);
 
 /*
+ * ReduceScatter (sum) over R emulated ranks — the two-shot's first half as a
+ * standard collective (the pages' library implements the standard
+ * collective API: MSCCL++ ASPLOS'26 abstract).
+ *   inputs    : host array of nranks device pointers; inputs[p] holds
+ *               nranks * recvcount elements.  Read only; may alias each other.
+ *   outputs   : host array of nranks device pointers; outputs[r] receives
+ *               recvcount elements: element i is the sum over p of
+ *               inputs[p][r * recvcount + i], accumulated in binary32 in rank
+ *               order and rounded once (as mscl_allreduce).  outputs[r] may be
+ *               block r of inputs[r] (in place); otherwise outputs must not
+ *               overlap any input or each other.
+ *   recvcount : elements per output block; 0 is a no-op.
+ *   dtype, nranks, stream : as mscl_allreduce (a channel set for the current
+ *               device and nranks must exist).
+ * Pointers need element-size alignment.  When every block boundary is 16-byte
+ * aligned the data moves as 16-byte vectors, otherwise element by element.
+ * Each rank gets its block from every peer and writes only its own output, so
+ * the call runs no barrier.  Asynchronous, one kernel, no allocation.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
+ */
+mscl_status_t mscl_reduce_scatter(const void* const inputs[], void* const outputs[], size_t recvcount,
+                                  mscl_dtype_t dtype, int nranks, void* stream);
+
+/*
+ * AllGather over R emulated ranks — the two-shot's second half as a standard
+ * collective.
+ *   inputs    : host array of nranks device pointers; inputs[r] holds
+ *               sendcount elements.  Read only.
+ *   outputs   : host array of nranks device pointers; outputs[p] receives
+ *               nranks * sendcount elements: block r is a bit-for-bit copy of
+ *               inputs[r].  inputs[r] may be block r of outputs[r] (in place,
+ *               that block is then left as it is); otherwise inputs must not
+ *               overlap any output, and outputs must not overlap each other.
+ *   sendcount : elements per input block; 0 is a no-op.
+ *   dtype, nranks, stream : as mscl_allreduce.
+ * Each rank puts its block into every peer's output (a MemoryChannel put);
+ * the call's completion on the stream is the completion point.
+ * Pointers need element-size alignment (16-byte vectors when every block
+ * boundary allows).  Asynchronous, one kernel, no allocation.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
+ */
+mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], size_t sendcount,
+                             mscl_dtype_t dtype, int nranks, void* stream);
+
+/*
  * The algorithm MSCL_ALGO_AUTO resolves to for this size: one-shot when the
  * per-rank buffer (count * element size) is at most a threshold that falls
  * with R (measured crossovers on MI355X: no limit for R <= 2, 2 MiB for

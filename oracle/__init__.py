@@ -22,6 +22,11 @@ What it computes (plain definition, no blocking or reordering beyond it):
   element type (round-to-nearest-even, subnormals kept, NaN/Inf propagated).
   The result is replicated to all R outputs.
 
+The same module also defines the two halves of the collective as standard
+collectives of their own: ReduceScatter (rank r receives block r of the sum,
+same accumulation rule) and AllGather (every rank receives all ranks' blocks
+in rank order, bit for bit).
+
 Modules:
   allreduce.py      NumPy implementation (the authority).
   allreduce_cpu.c   The same definition in plain C over host threads, used

@@ -180,3 +180,26 @@ def ulp_distance(got: np.ndarray, want: np.ndarray, dtype: str) -> np.ndarray:
     d = np.where(gn & wn, 0, d)
     d = np.where(gn ^ wn, 1 << 40, d)
     return d
+
+
+def reduce_scatter(inputs, dtype: str) -> list:
+    """ReduceScatter (sum) of R buffers of R*c elements each: output r holds
+    elements [r*c, (r+1)*c) of the element-wise sum, accumulated and rounded
+    exactly as in `allreduce` (the standard collective that hands each rank
+    one block of the reduced result; MSCCL++ ASPLOS'26 abstract: a library
+    implementing the standard collective API)."""
+    _check_dtype(dtype)
+    R = len(inputs)
+    n = len(inputs[0])
+    if n % R:
+        raise ValueError("each input must hold R * recvcount elements")
+    c = n // R
+    return [round_to(accumulate_f32(inputs, dtype, r * c, (r + 1) * c), dtype) for r in range(R)]
+
+
+def allgather(inputs, dtype: str) -> list:
+    """AllGather of R buffers of c elements each: every output is rank 0's
+    buffer, then rank 1's, ..., then rank R-1's (R*c elements), bit for bit."""
+    _check_dtype(dtype)
+    joined = np.concatenate([np.asarray(x, dtype=STORAGE[dtype]) for x in inputs])
+    return [joined.copy() for _ in inputs]

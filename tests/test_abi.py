@@ -150,3 +150,65 @@ def test_channel_calls_reject_unknown_handles():
     assert lib.mscl_channel_create(17, 0, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
     assert lib.mscl_channel_create(4, -1, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
     assert lib.mscl_channel_create(4, 0, None) == M.ERR_INVALID_ARGUMENT
+
+
+# ---------------------------------------------------------------- ReduceScatter / AllGather validation
+
+@pytest.mark.parametrize("fn", ["raw_reduce_scatter", "raw_allgather"])
+def test_blocks_bad_arguments(fn):
+    call = getattr(M, fn)
+    ins, outs = addrs(4, A), addrs(4, A * 64)
+    assert call(ins, outs, 10, M.FLOAT32, 0, 0) == M.ERR_INVALID_ARGUMENT
+    assert call(ins, outs, 10, M.FLOAT32, 17, 0) == M.ERR_INVALID_ARGUMENT
+    assert call(ins, outs, 10, 3, 4, 0) == M.ERR_INVALID_ARGUMENT
+    assert call(None, outs, 10, M.FLOAT32, 4, 0) == M.ERR_INVALID_ARGUMENT
+    assert call(ins, None, 10, M.FLOAT32, 4, 0) == M.ERR_INVALID_ARGUMENT
+    bad = list(ins)
+    bad[1] = 0
+    assert call(bad, outs, 10, M.FLOAT32, 4, 0) == M.ERR_INVALID_ARGUMENT
+    assert call(ins, outs, 2 ** 62, M.FLOAT32, 4, 0) == M.ERR_INVALID_ARGUMENT
+    assert call(ins, outs, 0, M.FLOAT32, 4, 0) == M.SUCCESS  # no-op, nothing launched
+
+
+@pytest.mark.parametrize("fn", ["raw_reduce_scatter", "raw_allgather"])
+def test_blocks_element_alignment(fn):
+    call = getattr(M, fn)
+    ins, outs = addrs(2, A), addrs(2, A * 64)
+    odd = list(ins)
+    odd[0] += 2  # 2-byte aligned: fine for bf16 (would need a GPU), wrong for fp32
+    assert call(odd, outs, 8, M.FLOAT32, 2, 0) == M.ERR_MISALIGNED
+    odd = list(outs)
+    odd[1] += 1
+    assert call(ins, odd, 8, M.BFLOAT16, 2, 0) == M.ERR_MISALIGNED
+
+
+def test_reduce_scatter_overlaps():
+    R, rc = 3, 256  # fp32: blocks of 1 KiB, inputs of 3 KiB
+    blk = rc * 4
+    ins = [A + r * 0x10000 for r in range(R)]
+    outs = [A * 64 + r * 0x10000 for r in range(R)]
+    outs2 = list(outs)
+    outs2[1] = outs2[0] + blk // 2  # outputs overlap each other
+    assert M.raw_reduce_scatter(ins, outs2, rc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
+    outs2 = list(outs)
+    outs2[0] = ins[1]  # output inside another rank's input
+    assert M.raw_reduce_scatter(ins, outs2, rc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
+    outs2 = list(outs)
+    outs2[2] = ins[2] + 1 * blk  # own input, but not block 2
+    assert M.raw_reduce_scatter(ins, outs2, rc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
+
+
+def test_allgather_overlaps():
+    R, sc = 3, 256
+    blk = sc * 4
+    ins = [A + r * 0x10000 for r in range(R)]
+    outs = [A * 64 + r * 0x10000 for r in range(R)]
+    outs2 = list(outs)
+    outs2[2] = outs2[1] + blk  # outputs (3 KiB each) overlap
+    assert M.raw_allgather(ins, outs2, sc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
+    ins2 = list(ins)
+    ins2[0] = outs[1]  # input inside another rank's output
+    assert M.raw_allgather(ins2, outs, sc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
+    ins2 = list(ins)
+    ins2[1] = outs[1]  # own output, but block 0 instead of block 1
+    assert M.raw_allgather(ins2, outs, sc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
