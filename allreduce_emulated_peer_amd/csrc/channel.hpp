@@ -114,9 +114,17 @@ struct RankChannels {
   // pure rendezvous (arrival-only signal, no acquire) for protocols in which
   // no data crosses ranks at this point; on MI355X it saves the per-workgroup
   // L2 write-back and invalidate, 6-10 us per launch.
+  //
+  // The ordered form fences every thread, not only the signalling wave: on
+  // gfx950 a workgroup barrier does not wait for the other waves' global
+  // loads and stores to complete, and the signalling wave's release covers
+  // only its own, so a peer on another XCD could otherwise see the signal
+  // before a sibling wave's stores reached memory (found by
+  // mscl_channel_selftest: a few stale words per 10^5).
   template <bool kOrdered>
   __device__ void barrier_all() const {
-    __syncthreads();  // every local thread's earlier accesses are done
+    if (kOrdered) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's accesses, published
+    __syncthreads();  // every local thread has reached the barrier
     if (threadIdx.x < 64) {
       const int peer = threadIdx.x;
       uint32_t* consumed = ch.consumed + static_cast<uint64_t>(rank) * ch.slots + slot;
@@ -134,6 +142,7 @@ struct RankChannels {
       if (peer == 0) __hip_atomic_store(consumed, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();  // the rest of the workgroup is now synchronised with the peers
+    if (kOrdered) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // and sees what they published
   }
 };
 

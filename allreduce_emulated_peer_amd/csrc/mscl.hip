@@ -521,6 +521,53 @@ __global__ __launch_bounds__(kThreads) void mscl_allgather_kernel(KernelArgs a) 
 }
 
 // ----------------------------------------------------------------------------
+// Channel self-test: the pages' signal/wait contract checked directly.  Every
+// round, each (rank, slot) workgroup writes a 4 KiB mailbox, runs the ordered
+// barrier, reads the mailbox of the next rank's same slot (a workgroup on a
+// different XCD) and counts words that differ from what that peer wrote
+// before it signalled; a second ordered barrier keeps the peer from
+// overwriting its mailbox before the reads are done.
+// ----------------------------------------------------------------------------
+
+constexpr int kSelftestWords = 1024;  // u32 words per mailbox (4 per lane)
+
+__device__ inline uint32_t selftest_word(uint32_t round, int rank, int slot, int i) {
+  uint32_t h = round * 0x9E3779B1u ^ (static_cast<uint32_t>(rank) << 24) ^ (static_cast<uint32_t>(slot) << 12) ^
+               static_cast<uint32_t>(i);
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  return h;
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void mscl_channel_selftest_kernel(KernelArgs a, uint32_t* mailbox,
+                                                                          uint32_t rounds, uint32_t* mismatches) {
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const RankChannels chans{a.ch, R, rank, slot};
+  const int peer = (rank + 1) % R;
+  uint32_t* mine = mailbox + (static_cast<uint64_t>(rank) * a.nblk + slot) * kSelftestWords;
+  const uint32_t* theirs = mailbox + (static_cast<uint64_t>(peer) * a.nblk + slot) * kSelftestWords;
+  uint32_t bad = 0;
+  for (uint32_t k = 0; k < rounds; ++k) {
+#pragma unroll
+    for (int j = 0; j < kSelftestWords / kThreads; ++j) {
+      const int i = j * kThreads + threadIdx.x;
+      mine[i] = selftest_word(k, rank, slot, i);
+    }
+    chans.template barrier_all<true>();
+#pragma unroll
+    for (int j = 0; j < kSelftestWords / kThreads; ++j) {
+      const int i = j * kThreads + threadIdx.x;
+      bad += theirs[i] != selftest_word(k, peer, slot, i);
+    }
+    chans.template barrier_all<true>();
+  }
+  if (bad) __hip_atomic_fetch_add(mismatches, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------------------
 // Kernel tables
 // ----------------------------------------------------------------------------
 
@@ -1101,6 +1148,62 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
   a.nblk = blocks_for(b.ch, sendcount, dtype, nranks, vec, /*gather=*/true);
   a.in_place_mask = mask;
   return launch(vec ? kAllGatherVec : kAllGatherElem, dtype, nranks, a, stream);
+}
+
+mscl_status_t mscl_channel_selftest(mscl_channel_t ch, uint32_t rounds, uint64_t* mismatches) {
+  if (!mismatches) return fail(MSCL_ERR_INVALID_ARGUMENT, "mismatches is null");
+  *mismatches = 0;
+  Bound b;
+  {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+    b.ch = ch;
+    b.timeout_us = ch->wait_timeout_us ? ch->wait_timeout_us : config().wait_timeout_us;
+    b.drop_rank = ch->drop_rank;
+  }
+  if (__atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE) != MSCL_SUCCESS)
+    return fail(MSCL_ERR_TIMEOUT, "an earlier call timed out; call mscl_channel_reset");
+  if (rounds == 0) return MSCL_SUCCESS;
+  const int R = ch->nranks;
+  KernelArgs a;
+  const void* none_in[kMaxRanks] = {};
+  void* none_out[kMaxRanks] = {};
+  fill_args(&a, b, none_in, none_out, R, 0);
+  a.nblk = std::max<uint32_t>(1, std::min<uint32_t>(ch->slots, static_cast<uint32_t>(ch->cus / R)));
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  hipError_t e = hipSetDevice(ch->device);
+  uint32_t* mailbox = nullptr;
+  uint32_t* counter = nullptr;
+  const size_t mb_bytes = sizeof(uint32_t) * kSelftestWords * R * a.nblk;
+  if (e == hipSuccess) e = hipMalloc(&mailbox, mb_bytes);
+  if (e == hipSuccess) e = hipMalloc(&counter, sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMemset(counter, 0, sizeof(uint32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) {
+    using SelftestFn = void (*)(KernelArgs, uint32_t*, uint32_t, uint32_t*);
+    SelftestFn table[kMaxRanks] = {
+        &mscl_channel_selftest_kernel<1>,  &mscl_channel_selftest_kernel<2>,  &mscl_channel_selftest_kernel<3>,
+        &mscl_channel_selftest_kernel<4>,  &mscl_channel_selftest_kernel<5>,  &mscl_channel_selftest_kernel<6>,
+        &mscl_channel_selftest_kernel<7>,  &mscl_channel_selftest_kernel<8>,  &mscl_channel_selftest_kernel<9>,
+        &mscl_channel_selftest_kernel<10>, &mscl_channel_selftest_kernel<11>, &mscl_channel_selftest_kernel<12>,
+        &mscl_channel_selftest_kernel<13>, &mscl_channel_selftest_kernel<14>, &mscl_channel_selftest_kernel<15>,
+        &mscl_channel_selftest_kernel<16>};
+    void* kargs[] = {&a, &mailbox, &rounds, &counter};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(table[R - 1]), dim3(static_cast<unsigned>(R) * a.nblk),
+                        dim3(kThreads), kargs, 0, nullptr);
+  }
+  uint32_t host_count = 0;
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(&host_count, counter, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (mailbox) (void)hipFree(mailbox);
+  if (counter) (void)hipFree(counter);
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail_hip(e, "channel self-test");
+  *mismatches = host_count;
+  if (__atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE) != MSCL_SUCCESS)
+    return fail(MSCL_ERR_TIMEOUT, "a wait timed out during the self-test");
+  return MSCL_SUCCESS;
 }
 
 }  // extern "C"

@@ -40,7 +40,7 @@ EXPORTS = (
     "mscl_version", "mscl_status_string", "mscl_last_error_string", "mscl_channel_create",
     "mscl_channel_destroy", "mscl_channel_check", "mscl_channel_reset", "mscl_allreduce",
     "mscl_select_algo", "mscl_channel_plan", "mscl_channel_set_fault_controls", "mscl_reduce_scatter",
-    "mscl_allgather",
+    "mscl_allgather", "mscl_channel_selftest",
 )
 
 
@@ -90,6 +90,8 @@ def load(path: str = LIB_PATH):
     for name in ("mscl_reduce_scatter", "mscl_allgather"):
         getattr(lib, name).restype = c_int
         getattr(lib, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, vp]
+    lib.mscl_channel_selftest.restype = c_int
+    lib.mscl_channel_selftest.argtypes = [vp, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint64)]
     lib.mscl_select_algo.restype = c_int
     lib.mscl_select_algo.argtypes = [c_size, c_int, c_int, ctypes.POINTER(c_int)]
     lib.mscl_channel_plan.restype = c_int
@@ -179,6 +181,13 @@ def channel_reset(handle: int) -> None:
 def channel_set_fault_controls(handle: int, wait_timeout_us: int = 0, drop_signal_rank: int = -1) -> None:
     _check(load().mscl_channel_set_fault_controls(ctypes.c_void_p(handle), wait_timeout_us, drop_signal_rank),
            "mscl_channel_set_fault_controls")
+
+
+def channel_selftest(handle: int, rounds: int) -> int:
+    """mscl_channel_selftest: returns the number of mismatching words (expected 0)."""
+    out = ctypes.c_uint64()
+    _check(load().mscl_channel_selftest(ctypes.c_void_p(handle), rounds, ctypes.byref(out)), "mscl_channel_selftest")
+    return out.value
 
 
 def select_algo(count: int, dtype: int, nranks: int) -> int:

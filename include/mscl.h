@@ -243,6 +243,21 @@ mscl_status_t mscl_channel_plan(mscl_channel_t channel, size_t count, mscl_dtype
 mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t channel, uint64_t wait_timeout_us,
                                               int drop_signal_rank);
 
+/*
+ * Check the channel contract on the device (for tests and bring-up; it
+ * synchronises and allocates, unlike the collectives).  For `rounds` rounds,
+ * every (rank, slot) workgroup writes a 4 KiB mailbox, signals and waits on
+ * the ordered barrier, reads the mailbox of the next rank's same slot (a
+ * workgroup on another XCD for R > 1) and compares it with what that peer
+ * wrote before signalling — the pages' "signal: all previous memory
+ * operations are done" (MSCCL++ README, Key Concepts, Channels) — then runs a
+ * second barrier before the next round overwrites the mailbox.
+ *   mismatches : receives the number of 32-bit words read that differed
+ *                (0 when the channel keeps its promise).
+ * Errors: INVALID_ARGUMENT, TIMEOUT (a wait ran out of time), HIP.
+ */
+mscl_status_t mscl_channel_selftest(mscl_channel_t channel, uint32_t rounds, uint64_t* mismatches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,6 +145,9 @@ def test_channel_calls_reject_unknown_handles():
     assert lib.mscl_channel_set_fault_controls(bogus, 0, -1) == M.ERR_INVALID_ARGUMENT
     plan = M.Plan()
     assert lib.mscl_channel_plan(bogus, 10, 0, 0, 0, ctypes.byref(plan)) == M.ERR_INVALID_ARGUMENT
+    count = ctypes.c_uint64()
+    assert lib.mscl_channel_selftest(bogus, 10, ctypes.byref(count)) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_selftest(bogus, 10, None) == M.ERR_INVALID_ARGUMENT
     out = ctypes.c_void_p()
     assert lib.mscl_channel_create(0, 0, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
     assert lib.mscl_channel_create(17, 0, ctypes.byref(out)) == M.ERR_INVALID_ARGUMENT
