@@ -57,9 +57,9 @@ typedef enum {
   MSCL_ALGO_AUTO = 0,          /* one-shot up to a size threshold, two-shot above it */
   MSCL_ALGO_ONE_SHOT = 1,      /* every rank reads all R inputs and writes its own output */
   MSCL_ALGO_TWO_SHOT = 2,      /* reduce-scatter, device signal/wait barrier, all-gather put */
-  MSCL_ALGO_TWO_SHOT_FUSED = 3 /* reduce-scatter whose all-gather put goes out from registers,
-                                  then a completion signal/wait barrier (no re-read of the
-                                  reduced chunk) */
+  MSCL_ALGO_TWO_SHOT_FUSED = 3 /* reduce-scatter whose all-gather put goes out from registers
+                                  (no re-read of the reduced chunk, no barrier inside the call;
+                                  completion is the end of the call on the stream) */
 } mscl_algo_t;
 
 typedef int mscl_status_t;
@@ -216,7 +216,10 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
  * with R (measured crossovers on MI355X: no limit for R <= 2, 2 MiB for
  * R <= 4, 512 KiB for R <= 8, 128 KiB above), else two-shot.  Pure host
  * computation.  The environment variable MSCL_ONESHOT_MAX_BYTES (read once)
- * replaces the table with one threshold for every R.
+ * replaces the table with one threshold for every R.  This is the choice for
+ * out-of-place calls; for an in-place call (any outputs[r] == inputs[r]) AUTO
+ * always takes the two-shot, whose in-place cost equals its out-of-place
+ * cost, while the one-shot then needs an ordered barrier on every tile.
  * Errors: INVALID_ARGUMENT.
  */
 mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, mscl_algo_t* out);

@@ -250,22 +250,23 @@ def test_graph_capture_and_replay():
         del g
 
 
-@pytest.mark.parametrize("algo", [M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED])
-def test_timeout_is_reported_not_hung(algo):
+@pytest.mark.parametrize("algo,in_place", [(M.ALGO_TWO_SHOT, False), (M.ALGO_ONE_SHOT, True)])
+def test_timeout_is_reported_not_hung(algo, in_place):
     """Force a missing signal from the host (rank 1 skips signal()) with a
     2 ms bound on every wait(): the kernel must exit, the status must read
     TIMEOUT, further calls must refuse until reset, and a reset must bring
-    the channel back."""
+    the channel back.  Both barrier kinds: the two-shot's arrival-only one and
+    the in-place one-shot's ordered one."""
     R, n = 4, 100_000
     xs = P.rand_inputs(R, n, "fp32", seed=31)
     want = O.allreduce(xs, "fp32")
     h = G.channel(R)
     ins = [G.to_device(x, "fp32") for x in xs]
-    outs = [G.poison_like(t) for t in ins]
+    outs = ins if in_place else [G.poison_like(t) for t in ins]
     stream = torch.cuda.current_stream().cuda_stream
     M.channel_set_fault_controls(h, wait_timeout_us=2000, drop_signal_rank=1)
     try:
-        G.note("fault injection: rank 1 drops its signals, 2 ms wait bound")
+        G.note(f"fault injection: rank 1 drops its signals, 2 ms wait bound, algo {algo} in place {in_place}")
         M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.FLOAT32, R, algo, stream)
         torch.cuda.synchronize()
         assert M.channel_check(h) == M.ERR_TIMEOUT
@@ -276,9 +277,17 @@ def test_timeout_is_reported_not_hung(algo):
         M.channel_set_fault_controls(h, 0, -1)
         M.channel_reset(h)
     assert M.channel_check(h) == M.SUCCESS
-    outs = G.run(xs, "fp32", {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_TWO_SHOT_FUSED: "two_shot_fused"}[algo],
-                 dev_inputs=ins)
+    outs = G.run(xs, "fp32", {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_ONE_SHOT: "one_shot"}[algo], in_place=in_place)
     G.assert_matches_oracle(outs, want, "fp32", "after reset")
+
+
+def test_auto_in_place_takes_two_shot():
+    R, n = 8, 8192  # out of place AUTO would take the one-shot
+    xs = P.rand_inputs(R, n, "bf16", seed=41)
+    want = O.allreduce(xs, "bf16")
+    assert M.select_algo(n, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
+    outs = G.run(xs, "bf16", "auto", in_place=True)
+    G.assert_matches_oracle(outs, want, "bf16", "auto in place")
 
 
 def test_channel_registry():
@@ -313,6 +322,10 @@ def test_plan_geometry():
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 0
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
-    assert q.uses_barrier == 1
+    assert q.algo == M.ALGO_TWO_SHOT and q.uses_barrier == 1  # AUTO sends in-place calls to the two-shot
+    q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_ONE_SHOT, in_place=True)
+    assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 1
+    q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
+    assert q.uses_barrier == 0
     r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
     assert r16.chunk_elems % 8 == 0 and r16.chunk_elems * 16 >= W.ragged_outliers_bf16().count
