@@ -744,32 +744,35 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
   return MSCL_SUCCESS;
 }
 
-// Largest per-rank buffer for which AUTO picks the one-shot.  One-shot reads
-// R*S per rank (from cache while the buffers fit) against the two-shot's
-// S plus a barrier, so the crossover falls quickly with R.  Measured on
-// MI355X with bf16 buffers (device time per call, calls replayed from a
-// graph, one-shot with XCD-grouped ranks, two-shot with the arrival-only
-// barrier): at R = 2 the one-shot wins at every size (64 MiB per rank: 41 us
-// against 50 us); otherwise it wins up to 2 MiB at R = 4, 512 KiB at R = 8
-// and 128 KiB at R = 16.
+// AUTO's size bands, from device time per call (calls replayed from a graph)
+// on MI355X with bf16 buffers, for R = 2, 4, 8, 16:
+//   one-shot        up to oneshot_max_bytes(R): every size at R <= 2, 512 KiB
+//                   at R <= 4, 128 KiB at R <= 8, 64 KiB above (it reads R*S
+//                   per rank, from cache while the buffers fit);
+//   fused two-shot  up to 4 MiB: no barrier and no re-read, best in the middle
+//                   (R = 8, 1 MiB: 3.7 us against 5.2 two-shot, 6.4 one-shot);
+//   two-shot        above: its separate read and write phases stream HBM best
+//                   (R = 8, 128 MiB: 376 us against 381 fused).
+// In place, the one-shot would need an ordered barrier on every tile (a rank
+// overwrites an input its peers still read: R = 8, 512 KiB, 109 us), so
+// in-place calls skip the first band.
 size_t oneshot_max_bytes(int nranks) {
   const size_t env = config().oneshot_max_bytes;
   if (env != SIZE_MAX) return env;
   if (nranks <= 2) return SIZE_MAX;
-  if (nranks <= 4) return size_t(2) << 20;
-  if (nranks <= 8) return size_t(512) << 10;
-  return size_t(128) << 10;
+  if (nranks <= 4) return size_t(512) << 10;
+  if (nranks <= 8) return size_t(128) << 10;
+  return size_t(64) << 10;
 }
 
-// In place, the one-shot needs an ordered barrier between its loads and
-// stores on every tile (a rank overwrites an input its peers still read),
-// while the two-shot's in-place call costs the same as out of place; so AUTO
-// sends every in-place call to the two-shot (R = 8, 512 KiB: 4.4 us against
-// 109 us).
+constexpr size_t kFusedMaxBytes = size_t(4) << 20;
+
 mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo, bool in_place) {
   if (algo != MSCL_ALGO_AUTO) return static_cast<mscl_algo_t>(algo);
-  if (in_place && nranks > 1) return MSCL_ALGO_TWO_SHOT;
-  return count * elem_bytes(dtype) <= oneshot_max_bytes(nranks) ? MSCL_ALGO_ONE_SHOT : MSCL_ALGO_TWO_SHOT;
+  const size_t bytes = count * elem_bytes(dtype);
+  if (!in_place && bytes <= oneshot_max_bytes(nranks)) return MSCL_ALGO_ONE_SHOT;
+  if (nranks == 1) return MSCL_ALGO_ONE_SHOT;  // a copy (or nothing, in place)
+  return bytes <= kFusedMaxBytes ? MSCL_ALGO_TWO_SHOT_FUSED : MSCL_ALGO_TWO_SHOT;
 }
 
 void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t algo, bool in_place,

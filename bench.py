@@ -175,7 +175,7 @@ def main() -> int:
     outs = [torch.empty_like(t) for t in ins]
     call = caller(w, ins, outs)
     plan = M.channel_plan(M.channel_create(w.nranks, dev), w.count, M.BFLOAT16, M.ALGO_AUTO)
-    algo_name = {1: "one_shot", 2: "two_shot"}[plan.algo]
+    algo_name = {1: "one_shot", 2: "two_shot", 3: "two_shot_fused"}[plan.algo]
     log(f"[bench] plan: {algo_name}, {plan.workgroups_per_rank} workgroups/rank x {plan.threads_per_workgroup} "
         f"threads, {plan.vectors_per_thread} vectors/thread")
     for _ in range(args.warmup):

@@ -54,7 +54,7 @@ typedef enum {
 } mscl_dtype_t;
 
 typedef enum {
-  MSCL_ALGO_AUTO = 0,          /* one-shot up to a size threshold, two-shot above it */
+  MSCL_ALGO_AUTO = 0,          /* by size: one-shot, then fused two-shot, then two-shot */
   MSCL_ALGO_ONE_SHOT = 1,      /* every rank reads all R inputs and writes its own output */
   MSCL_ALGO_TWO_SHOT = 2,      /* reduce-scatter, device signal/wait barrier, all-gather put */
   MSCL_ALGO_TWO_SHOT_FUSED = 3 /* reduce-scatter whose all-gather put goes out from registers
@@ -211,15 +211,16 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
                              mscl_dtype_t dtype, int nranks, void* stream);
 
 /*
- * The algorithm MSCL_ALGO_AUTO resolves to for this size: one-shot when the
- * per-rank buffer (count * element size) is at most a threshold that falls
- * with R (measured crossovers on MI355X: no limit for R <= 2, 2 MiB for
- * R <= 4, 512 KiB for R <= 8, 128 KiB above), else two-shot.  Pure host
- * computation.  The environment variable MSCL_ONESHOT_MAX_BYTES (read once)
- * replaces the table with one threshold for every R.  This is the choice for
- * out-of-place calls; for an in-place call (any outputs[r] == inputs[r]) AUTO
- * always takes the two-shot, whose in-place cost equals its out-of-place
- * cost, while the one-shot then needs an ordered barrier on every tile.
+ * The algorithm MSCL_ALGO_AUTO resolves to for an out-of-place call of this
+ * size (bytes = count * element size), from crossovers measured on MI355X:
+ *   one-shot        bytes <= 512 KiB (R <= 4; every size at R <= 2),
+ *                   128 KiB (R <= 8), 64 KiB (R <= 16);
+ *   fused two-shot  bytes <= 4 MiB;
+ *   two-shot        above.
+ * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: the
+ * one-shot would need an ordered barrier on every tile.  Pure host
+ * computation.  MSCL_ONESHOT_MAX_BYTES (environment, read once) replaces the
+ * one-shot limit for every R.  mscl_channel_plan reports the in-place choice.
  * Errors: INVALID_ARGUMENT.
  */
 mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, mscl_algo_t* out);

@@ -113,20 +113,21 @@ def test_size_overflow():
 
 
 def test_selector():
-    # one-shot up to a threshold that falls with R, two-shot above
+    # one-shot up to a limit that falls with R, fused two-shot up to 4 MiB, two-shot above
     KiB, MiB = 1024, 1024 * 1024
-    for R, limit in ((3, 2 * MiB), (4, 2 * MiB), (5, 512 * KiB), (8, 512 * KiB), (9, 128 * KiB), (16, 128 * KiB)):
+    for R, limit in ((3, 512 * KiB), (4, 512 * KiB), (5, 128 * KiB), (8, 128 * KiB), (9, 64 * KiB), (16, 64 * KiB)):
         assert M.select_algo(1, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
-        assert M.select_algo(limit // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
+        assert M.select_algo(limit // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
         assert M.select_algo(limit // 4, M.FLOAT32, R) == M.ALGO_ONE_SHOT
-        assert M.select_algo(limit // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT
+        assert M.select_algo(limit // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT_FUSED
+        assert M.select_algo(2 * MiB, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED  # 4 MiB per rank
+        assert M.select_algo(2 * MiB + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
     for R in (1, 2):  # one-shot at every size
         assert M.select_algo(2 ** 40, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
     assert M.select_algo(4096, M.FLOAT32, 4) == M.ALGO_ONE_SHOT  # the 16 KiB integer workload
-    assert M.select_algo(32 * 8192, M.BFLOAT16, 8) == M.ALGO_ONE_SHOT  # 512 KiB decode shape
-    assert M.select_algo(32 * 8192 + 1, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
-    assert M.select_algo(64 * MiB, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT
+    assert M.select_algo(32 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT_FUSED  # 512 KiB decode shape
+    assert M.select_algo(8192 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT  # 128 MiB prefill shape
     with pytest.raises(M.MsclError):
         M.select_algo(10, 7, 8)
     with pytest.raises(M.MsclError):

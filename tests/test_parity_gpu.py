@@ -281,7 +281,7 @@ def test_timeout_is_reported_not_hung(algo, in_place):
     G.assert_matches_oracle(outs, want, "fp32", "after reset")
 
 
-def test_auto_in_place_takes_two_shot():
+def test_auto_in_place_skips_one_shot():
     R, n = 8, 8192  # out of place AUTO would take the one-shot
     xs = P.rand_inputs(R, n, "bf16", seed=41)
     want = O.allreduce(xs, "bf16")
@@ -322,7 +322,9 @@ def test_plan_geometry():
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 0
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
-    assert q.algo == M.ALGO_TWO_SHOT and q.uses_barrier == 1  # AUTO sends in-place calls to the two-shot
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.uses_barrier == 0  # in place skips the one-shot band
+    q = M.channel_plan(h, 8192 * 8192, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
+    assert q.algo == M.ALGO_TWO_SHOT and q.uses_barrier == 1
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_ONE_SHOT, in_place=True)
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 1
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
