@@ -18,8 +18,10 @@ N(0, 0.5)), inputs already resident in HBM.  Prints ONE JSON line:
                  replayed from a graph
 
 Options: --gpus N (only 1: the emulation runs on one GPU), --steps K,
---warmup W, --no-cpu-baseline, --sweep (per-size table to stderr),
---copy-calibration (also run a plain 1 GiB device copy, for counter scaling).
+--warmup W, --no-cpu-baseline, --sweep (per-size tables to stderr: R=8 bf16
+1 KiB..128 MiB and the R=8 fp16 uniform[-1,1] workload 1 KiB..256 MiB, every
+algorithm), --main-only (profiler runs), --copy-calibration (also run a
+plain 1 GiB device copy, for counter scaling).
 """
 
 from __future__ import annotations
@@ -234,6 +236,20 @@ def main() -> int:
         log(f"[bench] {dw.name}: p50 {p50:.2f} us, graph {dev_us:.2f} us/call, algbw {decode['algbw_GBps_graph']} GB/s")
         del di, do
 
+    ragged = None
+    if not args.main_only:
+        rw = W.ragged_outliers_bf16()
+        ri = device_inputs(rw)
+        ro = [torch.empty_like(t) for t in ri]
+        rplan = M.channel_plan(M.channel_create(rw.nranks, dev), rw.count, M.BFLOAT16, M.ALGO_AUTO)
+        t_r = graph_us(rw, ri, ro, M.ALGO_AUTO, reps=10)
+        ragged = {"workload": rw.name, "algo": {1: "one_shot", 2: "two_shot", 3: "two_shot_fused"}[rplan.algo],
+                  "us": round(t_r, 1), "algbw_GBps": round(rw.bytes_per_rank / t_r / 1e3, 1),
+                  "pct_hbm_peak": round(100 * rw.algorithmic_bytes / t_r / 1e3 / HBM_PEAK_GBPS, 1)}
+        log(f"[bench] {rw.name}: {t_r:.1f} us, {ragged['pct_hbm_peak']}% of HBM peak")
+        del ri, ro
+        torch.cuda.empty_cache()
+
     collectives = None
     if not args.main_only:
         # ReduceScatter of the prefill buffers (16 MiB blocks) and AllGather of
@@ -286,20 +302,24 @@ def main() -> int:
         torch.cuda.empty_cache()
 
     if args.sweep:
-        log("[bench] sweep R=8 bf16 (hot buffers, graph-replayed device time): bytes/rank, us one/two/fused, "
-            "best algbw GB/s, % HBM peak")
-        for k in range(10, 28):
-            sw = W.sweep_bf16(k)
-            si = device_inputs(sw)
-            so = [torch.empty_like(t) for t in si]
-            reps = 50 if sw.bytes_per_rank <= (4 << 20) else 5
-            t = {name: graph_us(sw, si, so, algo, reps) for algo, name in
-                 ((M.ALGO_ONE_SHOT, "one"), (M.ALGO_TWO_SHOT, "two"), (M.ALGO_TWO_SHOT_FUSED, "fused"))}
-            best = min(t.values())
-            log(f"[sweep] {sw.bytes_per_rank:>10d} {t['one']:9.2f} {t['two']:9.2f} {t['fused']:9.2f} "
-                f"{sw.bytes_per_rank / best / 1e3:8.1f} {100 * sw.algorithmic_bytes / best / 1e3 / HBM_PEAK_GBPS:6.1f}")
-            del si, so
-            torch.cuda.empty_cache()
+        sweeps = (("bf16", W.sweep_bf16, range(10, 28)), ("fp16", W.sweep_fp16, range(10, 29)))
+        for tag, make, ks in sweeps:
+            log(f"[bench] sweep R=8 {tag} (hot buffers, graph-replayed device time): bytes/rank, us one/two/fused, "
+                "best algbw GB/s, % HBM peak, AUTO's pick")
+            for k in ks:
+                sw = make(k)
+                si = device_inputs(sw)
+                so = [torch.empty_like(t) for t in si]
+                reps = 50 if sw.bytes_per_rank <= (4 << 20) else 5
+                t = {name: graph_us(sw, si, so, algo, reps) for algo, name in
+                     ((M.ALGO_ONE_SHOT, "one"), (M.ALGO_TWO_SHOT, "two"), (M.ALGO_TWO_SHOT_FUSED, "fused"))}
+                best = min(t.values())
+                pick = {1: "one", 2: "two", 3: "fused"}[M.select_algo(sw.count, code[sw.dtype], sw.nranks)]
+                log(f"[sweep-{tag}] {sw.bytes_per_rank:>10d} {t['one']:9.2f} {t['two']:9.2f} {t['fused']:9.2f} "
+                    f"{sw.bytes_per_rank / best / 1e3:8.1f} {100 * sw.algorithmic_bytes / best / 1e3 / HBM_PEAK_GBPS:6.1f}"
+                    f" {pick}")
+                del si, so
+                torch.cuda.empty_cache()
 
     if args.copy_calibration:
         nbytes = 1 << 30
@@ -347,6 +367,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "latency": latency,
         "decode_512KiB": decode,
+        "ragged_r16": ragged,
         "collectives": collectives,
     }
     print(json.dumps(line), flush=True)
