@@ -1,39 +1,42 @@
-// MemoryChannel-style AllReduce over R emulated peer ranks on one gfx950 GPU.
+// MemoryChannel-style collectives over R emulated peer ranks on one gfx950 GPU.
 //
 // The MSCCL++ pages present AllReduce as the collective their library speeds
 // up for tensor-parallel LLM serving (project summary, "Highlighted
 // Details"), built from GPU-side channel methods (README, Key Concepts,
 // "On-GPU Communication Interfaces: Channels") of which the MemoryChannel
 // moves data with many GPU threads loading and storing peer memory directly
-// ("PortChannel and MemoryChannel").  This file holds the two kernels and the
-// host side of the C ABI declared in include/mscl.h.
+// ("PortChannel and MemoryChannel").  This file holds the kernels and the
+// host side of the C ABI declared in include/mscl.h:
 //
-// Rank layout.  In the two-shot, workgroup w of a launch is emulated rank
-// (w % R), channel slot (w / R); with the hardware's round-robin dispatch of
-// workgroups over the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.
-// The one-shot groups instead the R ranks of a slot on one XCD, because there
-// every rank re-reads the same input lines.  Each
-// workgroup has 256 threads (4 wavefronts of 64); each thread keeps U
-// 16-byte vectors of each of the R rank buffers in flight per iteration.
+//   mscl_oneshot        every rank reads all R inputs and writes its own
+//                       output; in place, an ordered barrier separates each
+//                       tile's loads from its stores (a rank overwrites an
+//                       input its peers are still reading).
+//   mscl_twoshot        reduce-scatter (rank r reduces chunk r of all
+//                       inputs into its own output), an arrival-only
+//                       barrier, all-gather (rank r puts its chunk into every
+//                       peer's output).
+//   mscl_twoshot_fused  reduce-scatter whose result goes from registers
+//                       straight into every output; no barrier.
+//   mscl_reduce_scatter_kernel / mscl_allgather_kernel
+//                       the two halves as standard collectives.
+//   mscl_channel_selftest_kernel
+//                       the ordered barrier's publish/acquire contract.
 //
-// One-shot: every rank reads all R inputs over the whole buffer, reduces in
-// registers (binary32, rank order) and writes its own output.  When an output
-// is also an input (in place), the ranks' slot-b workgroups run the channel
-// barrier between their loads and their stores of each tile, because a
-// rank's stores overwrite an input its peers are still reading.
+// Rank layout.  Workgroup w of a launch is emulated rank (w % R), channel
+// slot (w / R); with the hardware's round-robin dispatch of workgroups over
+// the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.  The one-shot
+// instead groups the R ranks of a slot on one XCD, because there every rank
+// re-reads the same input lines.  Each workgroup has 256 threads (4
+// wavefronts of 64); a tile is U 16-byte vectors per lane.
 //
-// Two-shot: rank r owns chunk r = elements [r*c, min((r+1)*c, n)) with
-// c = roundup(ceil(n/R), V).  Reduce-scatter: rank r reads chunk r of all R
-// inputs and writes the reduced chunk to its own output.  Then the channel
-// barrier (signal every peer, wait for every peer).  All-gather: rank r puts
-// its reduced chunk into every peer's output, reading it back in reverse
-// tile order so the most recently written tiles are still in cache.  Each
-// thread handles the same vectors in both phases, which keeps in-place calls
-// safe: the only reader of in[p][chunk r] is rank r itself, earlier in the
-// same thread.
+// Two-shot chunks: rank r owns elements [r*c, min((r+1)*c, n)) with
+// c = roundup(ceil(n/R), V), V = 16 / element size.  Each lane handles the
+// same vectors in both phases, which keeps in-place calls safe: the only
+// reader of in[p][chunk r] is rank r itself, earlier, in the same lane.
 //
-// Both kernels add in rank order 0..R-1 starting from rank 0's value and
-// round once, so their results are bit-identical to each other.
+// Every reduction adds in rank order 0..R-1 starting from rank 0's value and
+// rounds once, so all algorithms give bit-identical results.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -318,12 +321,11 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
 // tile of chunk r and writes the rounded vector straight into every rank's
 // output (its own included), so the reduced chunk is never re-read and the
 // call moves exactly R*S bytes in and R*S out.  Inputs are read once and
-// outputs written once, so both stream past the caches.  The channel barrier
-// moves to the end, where it is the completion handshake of a put-based
-// exchange: signal() tells each peer "my puts into your output are done",
-// wait() collects the peers' signals for ours.  In place is safe without
-// ordering across ranks: the only reader of in[p][chunk r] is rank r, and
-// each lane loads a vector from every input before it stores that vector.
+// outputs written once, so both stream past the caches.  No barrier runs
+// inside the call: rank r writes only chunk r of every output, which no
+// other rank reads or writes during the call, and in place the only reader
+// of in[p][chunk r] is rank r itself, each lane loading a vector from every
+// input before it stores that vector.
 template <class C, int R, int U, bool kFull>
 __device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
@@ -1113,6 +1115,7 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
   bool in_place = false;
   mscl_status_t st = validate_call(inputs, outputs, count, dtype, nranks, algo, &in_place);
   if (st != MSCL_SUCCESS || count == 0) return st;
+  if (nranks == 1 && in_place) return MSCL_SUCCESS;  // the sum of one buffer is already in place
   Bound b;
   if ((st = bind_channel(nranks, &b)) != MSCL_SUCCESS) return st;
 

@@ -146,7 +146,8 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  *             reduced buffer (count elements).  outputs[r] may equal
  *             inputs[r] (in place); otherwise it must not overlap any input,
  *             and no two outputs may overlap.
- *   count   : elements per buffer; 0 is a no-op that launches nothing.
+ *   count   : elements per buffer; 0 is a no-op that launches nothing (as is
+ *             nranks == 1 in place).
  *   dtype   : element type of inputs and outputs.
  *   nranks  : R, 1..MSCL_MAX_RANKS; a channel set for (current device, R)
  *             must exist (mscl_channel_create).
