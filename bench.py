@@ -71,6 +71,34 @@ def committed_traffic():
     return float(t.group(1))
 
 
+def oracle_record() -> int:
+    """The oracle timed once per workload at its full size, for the record:
+    the NumPy oracle on one core and the plain-C oracle on up to 16 threads,
+    with the same algbw accounting (S / t)."""
+    from allreduce_emulated_peer_amd import workloads as W
+    from oracle import allreduce as O
+    from oracle import cpu as C
+
+    cores = min(os.cpu_count() or 1, 16)
+    rows = []
+    for w in (W.integer_small(), W.decode_bf16(), W.prefill_bf16(), W.sweep_fp16(25), W.ragged_outliers_bf16()):
+        xs = W.generate_all(w)
+        O.allreduce(xs, w.dtype)  # warm: the first pass pays the inputs' first-touch page faults
+        t1 = time.perf_counter()
+        O.allreduce(xs, w.dtype)
+        t_np = time.perf_counter() - t1
+        C.allreduce(xs, w.dtype, nthreads=cores)  # warm
+        t1 = time.perf_counter()
+        C.allreduce(xs, w.dtype, nthreads=cores)
+        t_c = time.perf_counter() - t1
+        rows.append({"workload": w.name, "numpy_s": round(t_np, 4), "numpy_algbw_GBps": round(w.bytes_per_rank / t_np / 1e9, 3),
+                     "c_s": round(t_c, 4), "c_algbw_GBps": round(w.bytes_per_rank / t_c / 1e9, 3)})
+        log(f"[oracle-record] {rows[-1]}")
+        del xs
+    print(json.dumps({"oracle_record": rows, "c_threads": cores, "cpu_count": os.cpu_count()}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,11 +110,15 @@ def main() -> int:
     ap.add_argument("--latency-iters", type=int, default=1000)
     ap.add_argument("--main-only", action="store_true",
                     help="time only the main workload (for profiler runs): no latency, decode or CPU legs")
+    ap.add_argument("--oracle-record", action="store_true",
+                    help="CPU only: time the NumPy oracle (one core) and the C oracle once per workload at full size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: the R emulated ranks all live on one GPU, "
               "and this build runs no multi-GPU path", file=sys.stderr)
         return 2
+    if args.oracle_record:
+        return oracle_record()
 
     import torch
 
@@ -224,17 +256,82 @@ def main() -> int:
     if latency:
         latency["note"] = ("p50_us: HIP events around each call, host launch cost included; "
                            "graph_us_per_call: 100 calls replayed from one graph (device time per call)")
+    host = None
+    if not args.main_only:
+        # Host cost of one call (ctypes + validation + launch), CPU clock over
+        # 10^4 back-to-back calls at 16 KiB; and of a call that launches
+        # nothing (count = 0), which isolates the launch itself.
+        hw = W.sweep_bf16(14)
+        hi_ = device_inputs(hw)
+        ho = [torch.empty_like(t) for t in hi_]
+        c16 = caller(hw, hi_, ho)
+        import dataclasses
+        c0 = caller(dataclasses.replace(hw, count=0), hi_, ho)
+        for c in (c16, c0):
+            for _ in range(100):
+                c()
+        torch.cuda.synchronize()
+        res = {}
+        for name, c in (("with_launch", c16), ("no_launch_count0", c0)):
+            t1 = time.perf_counter()
+            for _ in range(10000):
+                c()
+            res[name] = (time.perf_counter() - t1) / 10000 * 1e6
+            torch.cuda.synchronize()
+        host = {"us_per_call": round(res["with_launch"], 2), "us_per_call_count0": round(res["no_launch_count0"], 2),
+                "note": "CPU clock over 10^4 back-to-back calls from Python (ctypes), 16 KiB R=8 bf16"}
+        log(f"[bench] host cost: {host['us_per_call']} us per call, {host['us_per_call_count0']} us with count = 0")
+        del hi_, ho
+
     if not args.main_only:
         dw = W.decode_bf16()
         di = device_inputs(dw)
         do = [torch.empty_like(t) for t in di]
         p50, mean = p50_us(caller(dw, di, do), args.latency_iters)
         dev_us = graph_us(dw, di, do)
-        decode = {"workload": dw.name, "p50_us": round(p50, 2), "graph_us_per_call": round(dev_us, 2),
-                  "algbw_GBps_graph": round(dw.bytes_per_rank / dev_us / 1e3, 1),
-                  "cache": "hot (8 MiB footprint stays in cache)"}
-        log(f"[bench] {dw.name}: p50 {p50:.2f} us, graph {dev_us:.2f} us/call, algbw {decode['algbw_GBps_graph']} GB/s")
+        # Cold: rotate K buffer sets whose total footprint (K * 2RS = 512 MiB)
+        # exceeds the 256 MB Infinity Cache, so every call starts from HBM.
+        K = -(-(512 << 20) // (2 * dw.nranks * dw.bytes_per_rank))
+        sets = [(di, do)] + [([t.clone() for t in di], [torch.empty_like(t) for t in di]) for _ in range(K - 1)]
+        calls = [caller(dw, a, b) for a, b in sets]
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * K)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            calls[i % K]()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold_p50 = float(np.median([a.elapsed_time(b) * 1000.0 for a, b in ev]))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = [caller(dw, a, b, on_stream=torch.cuda.current_stream()) for a, b in sets]
+            for _ in range(2):
+                for c in cap:
+                    c()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold_dev = a.elapsed_time(b) * 1000.0 / (2 * K)
+        del g, sets, calls, cap
+        decode = {"workload": dw.name,
+                  "hot": {"p50_us": round(p50, 2), "graph_us_per_call": round(dev_us, 2),
+                          "algbw_GBps_graph": round(dw.bytes_per_rank / dev_us / 1e3, 1),
+                          "pct_hbm_peak_graph": round(100 * dw.algorithmic_bytes / dev_us / 1e3 / HBM_PEAK_GBPS, 1),
+                          "cache": "same buffers every call (8 MiB footprint stays in cache)"},
+                  "cold": {"p50_us": round(cold_p50, 2), "graph_us_per_call": round(cold_dev, 2),
+                           "algbw_GBps_graph": round(dw.bytes_per_rank / cold_dev / 1e3, 1),
+                           "pct_hbm_peak_graph": round(100 * dw.algorithmic_bytes / cold_dev / 1e3 / HBM_PEAK_GBPS, 1),
+                           "cache": f"{K} buffer sets rotated ({K * 2 * dw.nranks * dw.bytes_per_rank >> 20} MiB footprint)"}}
+        log(f"[bench] {dw.name}: hot p50 {p50:.2f} us, graph {dev_us:.2f} us/call; "
+            f"cold p50 {cold_p50:.2f} us, graph {cold_dev:.2f} us/call")
         del di, do
+        torch.cuda.empty_cache()
 
     ragged = None
     if not args.main_only:
@@ -366,6 +463,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "latency": latency,
+        "host_api": host,
         "decode_512KiB": decode,
         "ragged_r16": ragged,
         "collectives": collectives,
