@@ -216,3 +216,17 @@ def test_allgather_overlaps():
     ins2 = list(ins)
     ins2[1] = outs[1]  # own output, but block 0 instead of block 1
     assert M.raw_allgather(ins2, outs, sc, M.FLOAT32, R, 0) == M.ERR_INVALID_ARGUMENT
+
+
+def test_plain_c_consumer_links_and_loads():
+    """tests/c_abi_driver is built against include/mscl.h and libmscl.so with
+    gcc alone; it loads the library through its rpath from any directory."""
+    import subprocess
+
+    driver = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_driver")
+    assert os.path.exists(driver), "tests/c_abi_driver is not built: run __graft_entry__.build()"
+    r = subprocess.run([driver, "--version"], capture_output=True, text=True, timeout=60, cwd="/")
+    assert r.returncode == 0 and r.stdout.strip() == f"mscl version {M.load().mscl_version()}"
+    r = subprocess.run([driver, "0", "2", "16", "0", "/nonexistent", "/nonexistent"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 1 and "bad R" in r.stderr
