@@ -10,10 +10,11 @@
 //                                    threads loading and storing directly.
 //   get                              the reverse direction: read the peer's
 //                                    memory directly.
-//   signal()                         tell the peer "I have arrived and all my
-//                                    earlier memory operations are done".
-//   flush()                          make earlier channel operations complete
-//                                    from the local device's point of view.
+//   signal()                         tell the peer this side has arrived and
+//                                    its earlier writes have completed.
+//   flush()                          wait until this side's earlier channel
+//                                    operations are finished as the local
+//                                    GPU sees them.
 //   wait()                           block until the peer has signalled.
 //   barrier                          signal, (flush,) wait, then a local
 //                                    workgroup barrier so the other local

@@ -2,9 +2,9 @@
  * mscl.h — C ABI of a MemoryChannel-style AllReduce over R emulated peer
  * ranks held in one AMD Instinct MI355X (gfx950).
  *
- * What is emulated.  The MSCCL++ pages describe a peer-to-peer connection
- * between two GPUs (a "channel") that is built on the host, copied to the GPU
- * at initialisation, and used from kernel code through device functions
+ * What is emulated.  The MSCCL++ pages build their communication on
+ * "channels": one GPU's link to one peer, set up by host code, handed to the
+ * GPU once at start-up, and driven from kernel code through device functions
  * put / get / signal / flush / wait (MSCCL++ README, Key Concepts, "On-GPU
  * Communication Interfaces: Channels").  A MemoryChannel moves data with GPU
  * threads reading and writing the peer's memory directly (same page,
@@ -101,8 +101,8 @@ const char* mscl_last_error_string(void);
  *   device : HIP device ordinal; must be a gfx950 GPU.
  *   out    : receives the handle (non-null).
  * The host builds the channel state once and the kernels receive it by value
- * at launch — the pages' "constructed by host-side interfaces and copied to
- * GPUs during initialization" (MSCCL++ README, Key Concepts, Channels).  State
+ * at launch, as the pages' channels are made by host code and handed to the
+ * GPU at start-up (MSCCL++ README, Key Concepts, Channels).  State
  * owned by the library: per (receiver rank, sender rank, slot) semaphore
  * counters and per (rank, slot) consumed-signal counters in device memory, a
  * status word in host-mapped memory, and the slot count derived from the
@@ -254,9 +254,9 @@ mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t channel, uint64_t w
  * every (rank, slot) workgroup writes a 4 KiB mailbox, signals and waits on
  * the ordered barrier, reads the mailbox of the next rank's same slot (a
  * workgroup on another XCD for R > 1) and compares it with what that peer
- * wrote before signalling — the pages' "signal: all previous memory
- * operations are done" (MSCCL++ README, Key Concepts, Channels) — then runs a
- * second barrier before the next round overwrites the mailbox.
+ * wrote before signalling, since the pages' signal promises that every write
+ * issued before it has completed (MSCCL++ README, Key Concepts, Channels);
+ * then it runs a second barrier before the next round overwrites the mailbox.
  *   mismatches : receives the number of 32-bit words read that differed
  *                (0 when the channel keeps its promise).
  * Errors: INVALID_ARGUMENT, TIMEOUT (a wait ran out of time), HIP.

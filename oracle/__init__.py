@@ -9,10 +9,10 @@ method's arithmetic.
 
 What it computes (plain definition, no blocking or reordering beyond it):
 
-* The pages name AllReduce as the collective MSCCL++ accelerates for
-  tensor-parallel LLM serving (MSCCL++ project summary, "Highlighted
-  Details"), and place it in a library implementing the standard collective
-  API (MSCCL++ ASPLOS'26 abstract).  A standard AllReduce with the sum
+* The pages name AllReduce as the collective MSCCL++ accelerates in
+  tensor-parallel LLM inference (MSCCL++ project summary, "Highlighted
+  Details"), inside a collective library with the usual collective
+  interface (MSCCL++ ASPLOS'26 abstract).  A standard AllReduce with the sum
   operator leaves every rank holding the element-wise sum of all ranks'
   buffers.
 * The pages fix no accumulation type, order or rounding.  Reading taken:

@@ -186,8 +186,8 @@ def reduce_scatter(inputs, dtype: str) -> list:
     """ReduceScatter (sum) of R buffers of R*c elements each: output r holds
     elements [r*c, (r+1)*c) of the element-wise sum, accumulated and rounded
     exactly as in `allreduce` (the standard collective that hands each rank
-    one block of the reduced result; MSCCL++ ASPLOS'26 abstract: a library
-    implementing the standard collective API)."""
+    one block of the reduced result; the MSCCL++ ASPLOS'26 abstract places
+    the method in a library offering the usual collective interface)."""
     _check_dtype(dtype)
     R = len(inputs)
     n = len(inputs[0])
