@@ -1,6 +1,7 @@
 """Build the HIP library libmscl.so in-tree for gfx950.
 
-One translation unit (csrc/mscl.hip: kernels + C ABI), compiled with hipcc:
+One translation unit (csrc/mscl.hip: the C ABI, including the kernels of
+csrc/kernels.hpp), compiled with hipcc:
 -O3, no fast-math, no FP contraction, packed-FP32 instructions disabled.
 """
 

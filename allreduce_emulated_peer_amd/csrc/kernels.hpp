@@ -1,0 +1,623 @@
+// MemoryChannel-style collectives over R emulated peer ranks on one gfx950 GPU.
+//
+// The MSCCL++ pages present AllReduce as the collective their library speeds
+// up for tensor-parallel LLM serving (project summary, "Highlighted
+// Details"), built from GPU-side channel methods (README, Key Concepts,
+// "On-GPU Communication Interfaces: Channels") of which the MemoryChannel
+// moves data with many GPU threads loading and storing peer memory directly
+// ("PortChannel and MemoryChannel").  This header holds the device side: the
+// kernels and the table the host code launches them from (mscl.hip holds
+// the host side of the C ABI declared in include/mscl.h):
+//
+//   mscl_oneshot        every rank reads all R inputs and writes its own
+//                       output; in place, an ordered barrier separates each
+//                       tile's loads from its stores (a rank overwrites an
+//                       input its peers are still reading).
+//   mscl_twoshot        reduce-scatter (rank r reduces chunk r of all
+//                       inputs into its own output), an arrival-only
+//                       barrier, all-gather (rank r puts its chunk into every
+//                       peer's output).
+//   mscl_twoshot_fused  reduce-scatter whose result goes from registers
+//                       straight into every output; no barrier.
+//   mscl_reduce_scatter_kernel / mscl_allgather_kernel
+//                       the two halves as standard collectives.
+//   mscl_channel_selftest_kernel
+//                       the ordered barrier's publish/acquire contract.
+//
+// Rank layout.  Workgroup w of a launch is emulated rank (w % R), channel
+// slot (w / R); with the hardware's round-robin dispatch of workgroups over
+// the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.  The one-shot
+// instead groups the R ranks of a slot on one XCD, because there every rank
+// re-reads the same input lines.  Each workgroup has 256 threads (4
+// wavefronts of 64); a tile is U 16-byte vectors per lane.
+//
+// Two-shot chunks: rank r owns elements [r*c, min((r+1)*c, n)) with
+// c = roundup(ceil(n/R), V), V = 16 / element size.  Each lane handles the
+// same vectors in both phases, which keeps in-place calls safe: the only
+// reader of in[p][chunk r] is rank r itself, earlier, in the same lane.
+//
+// Every reduction adds in rank order 0..R-1 starting from rank 0's value and
+// rounds once, so all algorithms give bit-identical results.
+
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <utility>
+
+#include "../../include/mscl.h"
+#include "channel.hpp"
+#include "codec.hpp"
+
+namespace mscl {
+
+constexpr int kThreads = 256;
+
+// gfx950 parts (MI350 series) have 8 accelerator complex dies (XCDs), each
+// with its own L2; the dispatcher deals workgroups to them round-robin, so
+// workgroup w runs on XCD w % 8.
+constexpr int kXcds = 8;
+
+// 16-byte vectors per thread per rank buffer per tile.  With the software
+// pipelining of the two-shot, one vector per rank buffer (R loads in flight
+// per lane, 2R while the next tile is prefetched) measured fastest for R >= 5
+// on MI355X; small R keeps 8+ loads in flight with two or four.
+template <int R>
+constexpr int unroll_for() {
+  return R <= 2 ? 4 : (R <= 4 ? 2 : 1);
+}
+
+struct KernelArgs {
+  const void* in[kMaxRanks];
+  void* out[kMaxRanks];
+  uint64_t count;  // elements per rank buffer
+  uint64_t chunk;  // two-shot: elements per rank chunk, a multiple of V
+  uint32_t nblk;   // workgroups (slots) per rank in this launch
+  uint32_t xcd_grouped;  // one-shot: all ranks of a slot on one XCD (needs nblk % 8 == 0)
+  uint32_t in_place_mask;  // allgather: bit r set when rank r's input already is its own output block
+  ChannelArgs ch;
+};
+
+// binary32 sum of one 16-byte vector position over the R ranks, in rank
+// order starting from rank 0's value, rounded once to the element type.
+template <class C, int R>
+__device__ inline u32x4 reduce_vec(const u32x4 (&x)[R]) {
+  float acc[C::V];
+  C::unpack(x[0], acc);
+#pragma unroll
+  for (int p = 1; p < R; ++p) {
+    float t[C::V];
+    C::unpack(x[p], t);
+#pragma unroll
+    for (int i = 0; i < C::V; ++i) acc[i] = acc[i] + t[i];
+  }
+  return C::pack(acc);
+}
+
+// The partial vector at the end of the buffer (n % V elements), reduced by
+// a single thread.
+template <class C, int R>
+__device__ inline u32x4 reduce_partial(const KernelArgs& a, uint64_t vi, int ntail) {
+  u32x4 x[R];
+#pragma unroll
+  for (int p = 0; p < R; ++p) x[p] = load_partial<C>(a.in[p], vi, ntail);
+  return reduce_vec<C, R>(x);
+}
+
+// A tile is U*256 consecutive 16-byte vectors: lane l of the workgroup takes
+// vectors base+l, base+256+l, ... so each wavefront instruction covers 1 KiB
+// contiguous.  Full tiles (kFull) need no bounds checks, which keeps every
+// load of the tile issued back to back; the last, partial tile re-reads the
+// range's last vector in lanes past the end and skips their stores.
+template <int R, int U, bool kFull, bool kStream>
+__device__ inline void load_tile(u32x4 (&x)[U][R], const void* const* src, uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
+#pragma unroll
+    for (int p = 0; p < R; ++p) x[u][p] = kStream ? load_vec_nt(src[p], vi) : load_vec(src[p], vi);
+  }
+}
+
+template <int U, bool kFull, bool kStream>
+__device__ inline void store_tile(void* dst, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (kFull || vi < vend) {
+      if (kStream)
+        store_vec_nt(dst, vi, y[u]);
+      else
+        store_vec(dst, vi, y[u]);
+    }
+  }
+}
+
+template <class C, int R, int U>
+__device__ inline void reduce_tile(u32x4 (&y)[U], const u32x4 (&x)[U][R]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) y[u] = reduce_vec<C, R>(x[u]);
+}
+
+// One tile of the one-shot: all R inputs -> own output, with the channel
+// barrier between loads and stores when running in place.
+template <class C, int R, int U, bool kInPlace, bool kFull>
+__device__ inline void oneshot_tile(const KernelArgs& a, const RankChannels& chans, void* dst, uint64_t base,
+                                    uint64_t vend) {
+  u32x4 x[U][R];
+  u32x4 y[U];
+  load_tile<R, U, kFull, false>(x, a.in, base, vend);  // every rank re-reads these: keep them cached
+  reduce_tile<C, R, U>(y, x);
+  // Peers read this rank's input until they signal; their loads must be
+  // complete before this rank overwrites it (write after read across ranks).
+  if constexpr (kInPlace) chans.template barrier_all<true>();
+  store_tile<U, kFull, false>(dst, y, base, vend);
+}
+
+template <class C, int R, bool kInPlace>
+__global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
+  constexpr int V = C::V;
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  // Every rank reads the same tile of all R inputs.  Putting the R ranks'
+  // workgroups of one slot on the same XCD lets that XCD's L2 serve the R-fold
+  // re-reads of each line (measured: R = 8 at 1 MiB per rank, 12.2 -> 6.6 us).
+  const int w = blockIdx.x;
+  const int rank = a.xcd_grouped ? (w / kXcds) % R : w % R;
+  const int slot = a.xcd_grouped ? (w / kXcds / R) * kXcds + w % kXcds : w / R;
+  const uint64_t n = a.count;
+  const uint64_t nfull = n / V;
+  const int ntail = static_cast<int>(n % V);
+  const uint64_t ntiles = (nfull + kTile - 1) / kTile;
+  const RankChannels chans{a.ch, R, rank, slot};
+  void* const dst = a.out[rank];
+
+  for (uint64_t t = slot; t < ntiles; t += a.nblk) {
+    const uint64_t base = t * kTile + threadIdx.x;
+    if ((t + 1) * kTile <= nfull)
+      oneshot_tile<C, R, U, kInPlace, true>(a, chans, dst, base, nfull);
+    else
+      oneshot_tile<C, R, U, kInPlace, false>(a, chans, dst, base, nfull);
+  }
+
+  if (ntail != 0 && slot == 0) {
+    u32x4 y = {0u, 0u, 0u, 0u};
+    if (threadIdx.x == 0) y = reduce_partial<C, R>(a, nfull, ntail);
+    if constexpr (kInPlace) chans.template barrier_all<true>();
+    if (threadIdx.x == 0) store_partial<C>(dst, nfull, y, ntail);
+  }
+}
+
+// Cache policy of the two-shot: inputs are read exactly once and the peers'
+// outputs written exactly once, so both stream past the caches; the rank's
+// own reduced chunk is written and read back, so it stays cacheable.
+constexpr bool kStreamRsLoads = true;
+constexpr bool kStreamAgStores = true;
+
+template <int R, int U, bool kFull>
+__device__ inline void ag_store(const KernelArgs& a, int rank, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int p = 0; p < R; ++p)  // put() to every peer, written once
+    if (p != rank) store_tile<U, kFull, kStreamAgStores>(a.out[p], y, base, vend);
+}
+
+template <int U, bool kFull>
+__device__ inline void ag_load(u32x4 (&y)[U], const void* mine, uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
+    y[u] = load_vec(mine, vi);
+  }
+}
+
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
+  constexpr int V = C::V;
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t B = a.nblk;
+  const uint64_t n = a.count;
+  const uint64_t lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, n);
+  const uint64_t hi = std::min<uint64_t>(lo + a.chunk, n);
+  const uint64_t v_lo = lo / V;    // chunk starts are multiples of V
+  const uint64_t v_full = hi / V;  // end of the chunk's full vectors
+  // nonzero only for the non-empty chunk that holds the buffer's end
+  const int ntail = hi > lo ? static_cast<int>(hi % V) : 0;
+  const uint64_t nv = v_full - v_lo;
+  // Tiles t = slot, slot + B, ... belong to this slot.  Tiles below
+  // `nfull_tiles` lie wholly inside the chunk; at most one partial tile
+  // (index nfull_tiles) follows.
+  const uint64_t nfull_tiles = nv / kTile;
+  const bool owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(nfull_tiles % B);
+  const RankChannels chans{a.ch, R, rank, slot};
+  void* const mine = a.out[rank];
+  const uint64_t lane_base = v_lo + threadIdx.x;
+
+  // Reduce-scatter: chunk `rank` of every input -> own output.  Software
+  // pipelined: the loads of the slot's next tile are issued before the
+  // current tile is reduced and stored, so each wave keeps R*U 16-byte
+  // loads in flight while it computes.
+  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+    uint64_t t = slot;
+    u32x4 cur[U][R];
+    load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * kTile, v_full);
+    while (true) {
+      const uint64_t tn = t + B;
+      const bool more = tn < nfull_tiles;
+      u32x4 nxt[U][R];
+      if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, v_full);
+      u32x4 y[U];
+      reduce_tile<C, R, U>(y, cur);
+      store_tile<U, true, false>(mine, y, lane_base + t * kTile, v_full);  // re-read by the all-gather: cached
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
+      t = tn;
+    }
+  }
+  if (owns_partial_tile) {
+    u32x4 x[U][R];
+    u32x4 y[U];
+    const uint64_t base = lane_base + nfull_tiles * kTile;
+    load_tile<R, U, false, kStreamRsLoads>(x, a.in, base, v_full);
+    reduce_tile<C, R, U>(y, x);
+    store_tile<U, false, false>(mine, y, base, v_full);
+  }
+  const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
+  if (tail_owner) store_partial<C>(mine, v_full, reduce_partial<C, R>(a, v_full, ntail), ntail);
+
+  // signal / wait with the same slot of every peer rank.  Arrival only: no
+  // data crosses ranks here.  The all-gather below reads only vectors this
+  // lane itself wrote above (program order), and writes peer locations that
+  // no peer reads during this call (rank p reads only its own chunk of every
+  // input, and in place rank r alone reads in[p][chunk r], earlier, in this
+  // lane).  Publishing or acquiring memory here would only cost an L2
+  // write-back and invalidate per workgroup.
+  chans.template barrier_all<false>();
+
+  // All-gather: put the reduced chunk into every peer's output, newest tiles
+  // first (they are the likeliest to still be in cache), again pipelined one
+  // tile ahead.  The same workgroup handles the same vectors as in the
+  // reduce-scatter, so in-place calls stay safe.
+  if (tail_owner) {
+    const u32x4 y = load_partial<C>(mine, v_full, ntail);
+    put_to_peers<C, R>(a.out, rank, v_full, y, v_full, ntail);
+  }
+  if (owns_partial_tile) {
+    u32x4 y[U];
+    const uint64_t base = lane_base + nfull_tiles * kTile;
+    ag_load<U, false>(y, mine, base, v_full);
+    ag_store<R, U, false>(a, rank, y, base, v_full);
+  }
+  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+    uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
+    u32x4 cur[U];
+    ag_load<U, true>(cur, mine, lane_base + t * kTile, v_full);
+    while (true) {
+      const bool more = t >= static_cast<uint64_t>(slot) + B;
+      const uint64_t tn = more ? t - B : t;
+      u32x4 nxt[U];
+      if (more) ag_load<U, true>(nxt, mine, lane_base + tn * kTile, v_full);
+      ag_store<R, U, true>(a, rank, cur, lane_base + t * kTile, v_full);
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      t = tn;
+    }
+  }
+}
+
+// Two-shot with the all-gather put issued from registers: rank r reduces each
+// tile of chunk r and writes the rounded vector straight into every rank's
+// output (its own included), so the reduced chunk is never re-read and the
+// call moves exactly R*S bytes in and R*S out.  Inputs are read once and
+// outputs written once, so both stream past the caches.  No barrier runs
+// inside the call: rank r writes only chunk r of every output, which no
+// other rank reads or writes during the call, and in place the only reader
+// of in[p][chunk r] is rank r itself, each lane loading a vector from every
+// input before it stores that vector.
+template <class C, int R, int U, bool kFull>
+__device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+#pragma unroll
+  for (int p = 0; p < R; ++p) store_tile<U, kFull, true>(a.out[p], y, base, vend);
+}
+
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
+  constexpr int V = C::V;
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t B = a.nblk;
+  const uint64_t n = a.count;
+  const uint64_t lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, n);
+  const uint64_t hi = std::min<uint64_t>(lo + a.chunk, n);
+  const uint64_t v_lo = lo / V;
+  const uint64_t v_full = hi / V;
+  const int ntail = hi > lo ? static_cast<int>(hi % V) : 0;
+  const uint64_t nv = v_full - v_lo;
+  const uint64_t nfull_tiles = nv / kTile;
+  const bool owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(nfull_tiles % B);
+  const RankChannels chans{a.ch, R, rank, slot};
+  const uint64_t lane_base = v_lo + threadIdx.x;
+
+  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+    uint64_t t = slot;
+    u32x4 cur[U][R];
+    load_tile<R, U, true, true>(cur, a.in, lane_base + t * kTile, v_full);
+    while (true) {
+      const uint64_t tn = t + B;
+      const bool more = tn < nfull_tiles;
+      u32x4 nxt[U][R];
+      if (more) load_tile<R, U, true, true>(nxt, a.in, lane_base + tn * kTile, v_full);
+      u32x4 y[U];
+      reduce_tile<C, R, U>(y, cur);
+      put_all_tile<C, R, U, true>(a, y, lane_base + t * kTile, v_full);
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
+      t = tn;
+    }
+  }
+  if (owns_partial_tile) {
+    u32x4 x[U][R];
+    u32x4 y[U];
+    const uint64_t base = lane_base + nfull_tiles * kTile;
+    load_tile<R, U, false, true>(x, a.in, base, v_full);
+    reduce_tile<C, R, U>(y, x);
+    put_all_tile<C, R, U, false>(a, y, base, v_full);
+  }
+  if (ntail != 0 && slot == 0 && threadIdx.x == 0) {
+    const u32x4 y = reduce_partial<C, R>(a, v_full, ntail);
+#pragma unroll
+    for (int p = 0; p < R; ++p) store_partial<C>(a.out[p], v_full, y, ntail);
+  }
+
+  // Completion is the end of the kernel on the stream: nothing inside the
+  // call reads the outputs.  (Across GPUs this is where each rank would
+  // signal "my puts into your output are done" and wait for its peers'; on
+  // one GPU an in-kernel ordered handshake measured 20-30 us per call for no
+  // observer.)
+}
+
+// ----------------------------------------------------------------------------
+// ReduceScatter and AllGather: the two halves of the two-shot as standard
+// collectives of their own (the pages' library implements the standard
+// collective API; MSCCL++ ASPLOS'26 abstract).
+//
+// ReduceScatter: rank r gets block r (recvcount elements) of every input and
+// writes the reduced block to its own output.  Rank r writes nothing a peer
+// reads and reads nothing a peer writes, so no barrier is needed inside the
+// call; stream order stands in for the start and end synchronisation.
+// AllGather: rank r puts its input into block r of every rank's output
+// (skipping its own when that block already is its input, in place).  Each
+// rank's puts go to a block no other rank writes, and the call's end on the
+// stream is the completion point.
+//
+// kVec: every block boundary is 16-byte aligned, so blocks move as 16-byte
+// vectors; otherwise one element per lane per step (coalesced 2- or 4-byte
+// accesses).
+// ----------------------------------------------------------------------------
+
+template <class C, int R, bool kVec>
+__global__ __launch_bounds__(kThreads) void mscl_reduce_scatter_kernel(KernelArgs a) {
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t rc = a.count;  // elements per block
+  void* const dst = a.out[rank];
+  if constexpr (kVec) {
+    const uint64_t nv = rc / C::V;  // rc is a multiple of V here
+    const uint64_t src0 = static_cast<uint64_t>(rank) * nv;  // block start, in vectors
+    const uint64_t ntiles = (nv + kTile - 1) / kTile;
+    const void* src[R];
+#pragma unroll
+    for (int p = 0; p < R; ++p) src[p] = static_cast<const u32x4*>(a.in[p]) + src0;
+    for (uint64_t t = slot; t < ntiles; t += a.nblk) {
+      const uint64_t base = t * kTile + threadIdx.x;
+      u32x4 x[U][R];
+      u32x4 y[U];
+      if ((t + 1) * kTile <= nv) {
+        load_tile<R, U, true, true>(x, src, base, nv);  // read once: streaming
+        reduce_tile<C, R, U>(y, x);
+        store_tile<U, true, false>(dst, y, base, nv);
+      } else {
+        load_tile<R, U, false, true>(x, src, base, nv);
+        reduce_tile<C, R, U>(y, x);
+        store_tile<U, false, false>(dst, y, base, nv);
+      }
+    }
+  } else {
+    using Bits = typename C::Bits;
+    const uint64_t off = static_cast<uint64_t>(rank) * rc;
+    for (uint64_t j = static_cast<uint64_t>(slot) * kThreads + threadIdx.x; j < rc;
+         j += static_cast<uint64_t>(a.nblk) * kThreads) {
+      float acc = C::widen(static_cast<const Bits*>(a.in[0])[off + j]);
+#pragma unroll
+      for (int p = 1; p < R; ++p) acc = acc + C::widen(static_cast<const Bits*>(a.in[p])[off + j]);
+      static_cast<Bits*>(dst)[j] = C::narrow(acc);
+    }
+  }
+}
+
+// AllGather keeps two vectors per lane in flight (it holds no R-fold
+// operands; one measured 337 us, four 267 us, two 243 us at R = 8 with 16 MiB
+// blocks) and loads the next tile while it stores the current one.
+constexpr int kAllGatherU = 2;
+
+template <int R>
+__device__ inline void allgather_store(const KernelArgs& a, int rank, bool skip_own, uint64_t dst0,
+                                       const u32x4 (&y)[kAllGatherU], uint64_t base, uint64_t nv, bool full) {
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    if (p == rank && skip_own) continue;
+    u32x4* out = static_cast<u32x4*>(a.out[p]) + dst0;  // put() into block `rank`
+#pragma unroll
+    for (int u = 0; u < kAllGatherU; ++u) {
+      const uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+      if (full || vi < nv) store_vec_nt(out, vi, y[u]);
+    }
+  }
+}
+
+__device__ inline void allgather_load(u32x4 (&y)[kAllGatherU], const void* src, uint64_t base, uint64_t nv,
+                                      bool full) {
+#pragma unroll
+  for (int u = 0; u < kAllGatherU; ++u) {
+    uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    if (!full) vi = std::min<uint64_t>(vi, nv - 1);
+    y[u] = load_vec(src, vi);  // cacheable: measured 185 us vs 243 us with streaming loads (R=8, 16 MiB blocks)
+  }
+}
+
+template <class C, int R, bool kVec>
+__global__ __launch_bounds__(kThreads) void mscl_allgather_kernel(KernelArgs a) {
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t sc = a.count;  // elements per input block
+  const void* const src = a.in[rank];
+  const bool skip_own = (a.in_place_mask >> rank) & 1u;
+  if constexpr (kVec) {
+    constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * kAllGatherU;
+    const uint64_t nv = sc / C::V;
+    const uint64_t dst0 = static_cast<uint64_t>(rank) * nv;
+    const uint64_t ntiles = (nv + kTile - 1) / kTile;
+    if (static_cast<uint64_t>(slot) >= ntiles) return;
+    uint64_t t = slot;
+    u32x4 cur[kAllGatherU];
+    allgather_load(cur, src, t * kTile + threadIdx.x, nv, (t + 1) * kTile <= nv);
+    while (true) {
+      const uint64_t tn = t + a.nblk;
+      const bool more = tn < ntiles;
+      u32x4 nxt[kAllGatherU];
+      if (more) allgather_load(nxt, src, tn * kTile + threadIdx.x, nv, (tn + 1) * kTile <= nv);
+      allgather_store<R>(a, rank, skip_own, dst0, cur, t * kTile + threadIdx.x, nv, (t + 1) * kTile <= nv);
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < kAllGatherU; ++u) cur[u] = nxt[u];
+      t = tn;
+    }
+  } else {
+    using Bits = typename C::Bits;
+    const uint64_t off = static_cast<uint64_t>(rank) * sc;
+    for (uint64_t j = static_cast<uint64_t>(slot) * kThreads + threadIdx.x; j < sc;
+         j += static_cast<uint64_t>(a.nblk) * kThreads) {
+      const Bits v = static_cast<const Bits*>(src)[j];
+#pragma unroll
+      for (int p = 0; p < R; ++p)
+        if (!(p == rank && skip_own)) static_cast<Bits*>(a.out[p])[off + j] = v;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Channel self-test: the pages' signal/wait contract checked directly.  Every
+// round, each (rank, slot) workgroup writes a 4 KiB mailbox, runs the ordered
+// barrier, reads the mailbox of the next rank's same slot (a workgroup on a
+// different XCD) and counts words that differ from what that peer wrote
+// before it signalled; a second ordered barrier keeps the peer from
+// overwriting its mailbox before the reads are done.
+// ----------------------------------------------------------------------------
+
+constexpr int kSelftestWords = 1024;  // u32 words per mailbox (4 per lane)
+
+__device__ inline uint32_t selftest_word(uint32_t round, int rank, int slot, int i) {
+  uint32_t h = round * 0x9E3779B1u ^ (static_cast<uint32_t>(rank) << 24) ^ (static_cast<uint32_t>(slot) << 12) ^
+               static_cast<uint32_t>(i);
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  return h;
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void mscl_channel_selftest_kernel(KernelArgs a, uint32_t* mailbox,
+                                                                          uint32_t rounds, uint32_t* mismatches) {
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const RankChannels chans{a.ch, R, rank, slot};
+  const int peer = (rank + 1) % R;
+  uint32_t* mine = mailbox + (static_cast<uint64_t>(rank) * a.nblk + slot) * kSelftestWords;
+  const uint32_t* theirs = mailbox + (static_cast<uint64_t>(peer) * a.nblk + slot) * kSelftestWords;
+  uint32_t bad = 0;
+  for (uint32_t k = 0; k < rounds; ++k) {
+#pragma unroll
+    for (int j = 0; j < kSelftestWords / kThreads; ++j) {
+      const int i = j * kThreads + threadIdx.x;
+      mine[i] = selftest_word(k, rank, slot, i);
+    }
+    chans.template barrier_all<true>();
+#pragma unroll
+    for (int j = 0; j < kSelftestWords / kThreads; ++j) {
+      const int i = j * kThreads + threadIdx.x;
+      bad += theirs[i] != selftest_word(k, peer, slot, i);
+    }
+    chans.template barrier_all<true>();
+  }
+  if (bad) __hip_atomic_fetch_add(mismatches, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------------------
+// Kernel tables
+// ----------------------------------------------------------------------------
+
+using KernelFn = void (*)(KernelArgs);
+enum {
+  kAlgoOneShot = 0,
+  kAlgoOneShotInPlace = 1,
+  kAlgoTwoShot = 2,
+  kAlgoTwoShotFused = 3,
+  kReduceScatterVec = 4,
+  kReduceScatterElem = 5,
+  kAllGatherVec = 6,
+  kAllGatherElem = 7
+};
+
+template <class C, int R>
+constexpr KernelFn kernel_for(int kind) {
+  switch (kind) {
+    case kAlgoOneShot: return &mscl_oneshot<C, R, false>;
+    case kAlgoOneShotInPlace: return &mscl_oneshot<C, R, true>;
+    case kAlgoTwoShot: return &mscl_twoshot<C, R>;
+    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R>;
+    case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
+    case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
+    case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;
+    case kAllGatherElem: return &mscl_allgather_kernel<C, R, false>;
+  }
+  return nullptr;
+}
+
+template <class C, int... Rs>
+KernelFn pick(int kind, int R, std::integer_sequence<int, Rs...>) {
+  KernelFn fn = nullptr;
+  ((R == Rs + 1 ? (fn = kernel_for<C, Rs + 1>(kind), 0) : 0), ...);
+  return fn;
+}
+
+inline KernelFn kernel_lookup(int kind, int dtype, int R) {
+  auto seq = std::make_integer_sequence<int, kMaxRanks>{};
+  switch (dtype) {
+    case MSCL_FLOAT32: return pick<F32>(kind, R, seq);
+    case MSCL_FLOAT16: return pick<F16>(kind, R, seq);
+    case MSCL_BFLOAT16: return pick<BF16>(kind, R, seq);
+  }
+  return nullptr;
+}
+
+inline int unroll_for_runtime(int R) { return R <= 2 ? 4 : (R <= 4 ? 2 : 1); }
+
+}  // namespace mscl

@@ -66,7 +66,7 @@ typedef int mscl_status_t;
 #define MSCL_SUCCESS 0
 #define MSCL_ERR_INVALID_ARGUMENT 1 /* a null/overlapping pointer, bad R, dtype, algo or size */
 #define MSCL_ERR_UNSUPPORTED 2      /* the device is not a gfx950 GPU */
-#define MSCL_ERR_MISALIGNED 3       /* a buffer is not 16-byte aligned */
+#define MSCL_ERR_MISALIGNED 3       /* a buffer is misaligned (16 bytes for allreduce, the element size for reduce-scatter and allgather) */
 #define MSCL_ERR_NOT_INITIALIZED 4  /* no channel set exists for (current device, R) */
 #define MSCL_ERR_OUT_OF_MEMORY 5    /* channel state could not be allocated */
 #define MSCL_ERR_HIP 6              /* a HIP runtime call or kernel launch failed */
