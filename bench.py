@@ -407,24 +407,59 @@ def main() -> int:
         torch.cuda.empty_cache()
 
     if args.sweep:
+        # Cold calls: a 768 MiB device copy (through the 256 MB Infinity Cache
+        # and every L2) runs before each call, and HIP events bracket the call
+        # alone.  The copy takes ~100 us, so the host is always ahead of the
+        # GPU and the event interval is the call's device time.  Sizes from
+        # 32 MiB per rank up are cold by construction (2RS >= 512 MiB).
+        fl_src = torch.empty(768 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        fl_dst = torch.empty_like(fl_src)
+
+        def cold_us(call, iters=15, flush_bytes=None):
+            src, dst = (fl_src, fl_dst) if flush_bytes is None else (fl_src[:flush_bytes], fl_dst[:flush_bytes])
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            torch.cuda.synchronize()
+            for a, b in ev:
+                dst.copy_(src)
+                a.record(stream)
+                call()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) * 1000.0 for a, b in ev]))
+
+        algos = ((M.ALGO_ONE_SHOT, "one"), (M.ALGO_TWO_SHOT, "two"), (M.ALGO_TWO_SHOT_FUSED, "fused"))
+        cw = W.sweep_bf16(10)
+        ci_, co_ = device_inputs(cw), None
+        co_ = [torch.empty_like(t) for t in ci_]
+        warm = cold_us(caller(cw, ci_, co_, M.ALGO_ONE_SHOT), iters=31, flush_bytes=1 << 20)
+        log(f"[bench] cold-method calibration: the 1 KiB one-shot bracketed the same way after a 1 MiB copy "
+            f"(its buffers stay cached): {warm:.2f} us; graph replay gives "
+            f"{graph_us(cw, ci_, co_, M.ALGO_ONE_SHOT, 50):.2f} us")
+        del ci_, co_
         sweeps = (("bf16", W.sweep_bf16, range(10, 28)), ("fp16", W.sweep_fp16, range(10, 29)))
         for tag, make, ks in sweeps:
-            log(f"[bench] sweep R=8 {tag} (hot buffers, graph-replayed device time): bytes/rank, us one/two/fused, "
-                "best algbw GB/s, % HBM peak, AUTO's pick")
+            log(f"[bench] sweep R=8 {tag}: bytes/rank; hot us one/two/fused (same buffers, graph-replayed device "
+                "time); best hot algbw GB/s and % HBM peak; AUTO's pick; cold us one/two/fused (caches flushed "
+                "before each call, below 32 MiB)")
             for k in ks:
                 sw = make(k)
                 si = device_inputs(sw)
                 so = [torch.empty_like(t) for t in si]
                 reps = 50 if sw.bytes_per_rank <= (4 << 20) else 5
-                t = {name: graph_us(sw, si, so, algo, reps) for algo, name in
-                     ((M.ALGO_ONE_SHOT, "one"), (M.ALGO_TWO_SHOT, "two"), (M.ALGO_TWO_SHOT_FUSED, "fused"))}
+                t = {name: graph_us(sw, si, so, algo, reps) for algo, name in algos}
                 best = min(t.values())
                 pick = {1: "one", 2: "two", 3: "fused"}[M.select_algo(sw.count, code[sw.dtype], sw.nranks)]
+                cold = ""
+                if sw.bytes_per_rank < (32 << 20):
+                    c = {name: cold_us(caller(sw, si, so, algo)) for algo, name in algos}
+                    cold = f"   cold {c['one']:9.2f} {c['two']:9.2f} {c['fused']:9.2f}"
                 log(f"[sweep-{tag}] {sw.bytes_per_rank:>10d} {t['one']:9.2f} {t['two']:9.2f} {t['fused']:9.2f} "
                     f"{sw.bytes_per_rank / best / 1e3:8.1f} {100 * sw.algorithmic_bytes / best / 1e3 / HBM_PEAK_GBPS:6.1f}"
-                    f" {pick}")
+                    f" {pick:5s}{cold}")
                 del si, so
                 torch.cuda.empty_cache()
+        del fl_src, fl_dst
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         nbytes = 1 << 30
