@@ -59,6 +59,9 @@ struct ChannelArgs {
   uint64_t timeout_ticks;  // bound of one wait(), in wall-clock ticks (100 MHz)
 };
 
+// What a barrier orders across ranks (see RankChannels::barrier_all).
+enum class Sync { kPublish, kAfterReads, kArrival };
+
 // The channels of rank `rank`'s slot `slot` to all of its peers.
 struct RankChannels {
   const ChannelArgs& ch;
@@ -109,22 +112,33 @@ struct RankChannels {
   // whole workgroup.  Lane p of wave 0 drives the channel to peer p, so the
   // R-1 signals and waits of a slot go out as one vector instruction each.
   //
-  // kOrdered = true is the pages' barrier: signal() publishes everything this
+  // Sync::kPublish is the pages' barrier: signal() publishes everything this
   // workgroup wrote before it, and an acquire after the waits makes what the
-  // peers wrote before their signals visible here.  kOrdered = false is a
-  // pure rendezvous (arrival-only signal, no acquire) for protocols in which
-  // no data crosses ranks at this point; on MI355X it saves the per-workgroup
-  // L2 write-back and invalidate, 6-10 us per launch.
+  // peers wrote before their signals visible here.  It fences every thread,
+  // not only the signalling wave: on gfx950 a workgroup barrier does not wait
+  // for the other waves' global loads and stores to complete, and the
+  // signalling wave's release covers only its own, so a peer on another XCD
+  // could otherwise see the signal before a sibling wave's stores reached
+  // memory (found by mscl_channel_selftest: a few stale words per 10^5).
   //
-  // The ordered form fences every thread, not only the signalling wave: on
-  // gfx950 a workgroup barrier does not wait for the other waves' global
-  // loads and stores to complete, and the signalling wave's release covers
-  // only its own, so a peer on another XCD could otherwise see the signal
-  // before a sibling wave's stores reached memory (found by
-  // mscl_channel_selftest: a few stale words per 10^5).
-  template <bool kOrdered>
+  // Sync::kAfterReads orders this workgroup's earlier loads before the
+  // peers' later stores (write after read across ranks, no data handed
+  // over): every thread waits until its own loads and stores have completed,
+  // then the signal goes out arrival-only and nothing is acquired.  A load
+  // that has returned its value cannot observe a store issued later, and a
+  // peer issues its stores only after its wait has seen this signal.  It
+  // skips kPublish's L2 write-back and invalidate, which on MI355X also
+  // discard the L2 lines every rank is re-reading.
+  //
+  // Sync::kArrival is a pure rendezvous (arrival-only signal, no waiting for
+  // earlier accesses, no acquire) for protocols in which no memory is shared
+  // across ranks at this point; on MI355X it saves the per-workgroup L2
+  // write-back and invalidate, 6-10 us per launch.
+  template <Sync kSync>
   __device__ void barrier_all() const {
+    constexpr bool kOrdered = kSync == Sync::kPublish;
     if (kOrdered) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's accesses, published
+    if (kSync == Sync::kAfterReads) __builtin_amdgcn_s_waitcnt(0);  // this thread's accesses, completed
     __syncthreads();  // every local thread has reached the barrier
     if (threadIdx.x < 64) {
       const int peer = threadIdx.x;

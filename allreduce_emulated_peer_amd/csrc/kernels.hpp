@@ -10,9 +10,10 @@
 // the host side of the C ABI declared in include/mscl.h):
 //
 //   mscl_oneshot        every rank reads all R inputs and writes its own
-//                       output; in place, an ordered barrier separates each
-//                       tile's loads from its stores (a rank overwrites an
-//                       input its peers are still reading).
+//                       output; in place, a barrier that waits for every
+//                       rank's loads of a tile separates them from the
+//                       tile's stores (a rank overwrites an input its peers
+//                       are still reading).
 //   mscl_twoshot        reduce-scatter (rank r reduces chunk r of all
 //                       inputs into its own output), an arrival-only
 //                       barrier, all-gather (rank r puts its chunk into every
@@ -22,7 +23,8 @@
 //   mscl_reduce_scatter_kernel / mscl_allgather_kernel
 //                       the two halves as standard collectives.
 //   mscl_channel_selftest_kernel
-//                       the ordered barrier's publish/acquire contract.
+//                       the barriers' publish/acquire and write-after-read
+//                       contracts.
 //
 // Rank layout.  Workgroup w of a launch is emulated rank (w % R), channel
 // slot (w / R); with the hardware's round-robin dispatch of workgroups over
@@ -143,19 +145,19 @@ __device__ inline void reduce_tile(u32x4 (&y)[U], const u32x4 (&x)[U][R]) {
   for (int u = 0; u < U; ++u) y[u] = reduce_vec<C, R>(x[u]);
 }
 
-// One tile of the one-shot: all R inputs -> own output, with the channel
-// barrier between loads and stores when running in place.
-template <class C, int R, int U, bool kInPlace, bool kFull>
-__device__ inline void oneshot_tile(const KernelArgs& a, const RankChannels& chans, void* dst, uint64_t base,
-                                    uint64_t vend) {
+// One tile of the one-shot: all R inputs reduced into this lane's vectors.
+template <class C, int R, int U, bool kFull>
+__device__ inline void oneshot_reduce(u32x4 (&y)[U], const KernelArgs& a, uint64_t base, uint64_t vend) {
   u32x4 x[U][R];
-  u32x4 y[U];
   load_tile<R, U, kFull, false>(x, a.in, base, vend);  // every rank re-reads these: keep them cached
   reduce_tile<C, R, U>(y, x);
-  // Peers read this rank's input until they signal; their loads must be
-  // complete before this rank overwrites it (write after read across ranks).
-  if constexpr (kInPlace) chans.template barrier_all<true>();
-  store_tile<U, kFull, false>(dst, y, base, vend);
+}
+
+// In place, tiles reduced per barrier: up to 8 vectors per lane are held in
+// registers between a batch's loads and its stores.
+template <int U>
+constexpr int inplace_batch() {
+  return 8 / U > 0 ? 8 / U : 1;
 }
 
 template <class C, int R, bool kInPlace>
@@ -169,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
   const int w = blockIdx.x;
   const int rank = a.xcd_grouped ? (w / kXcds) % R : w % R;
   const int slot = a.xcd_grouped ? (w / kXcds / R) * kXcds + w % kXcds : w / R;
+  const uint64_t B = a.nblk;
   const uint64_t n = a.count;
   const uint64_t nfull = n / V;
   const int ntail = static_cast<int>(n % V);
@@ -176,18 +179,53 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
   const RankChannels chans{a.ch, R, rank, slot};
   void* const dst = a.out[rank];
 
-  for (uint64_t t = slot; t < ntiles; t += a.nblk) {
-    const uint64_t base = t * kTile + threadIdx.x;
-    if ((t + 1) * kTile <= nfull)
-      oneshot_tile<C, R, U, kInPlace, true>(a, chans, dst, base, nfull);
-    else
-      oneshot_tile<C, R, U, kInPlace, false>(a, chans, dst, base, nfull);
+  if constexpr (!kInPlace) {
+    for (uint64_t t = slot; t < ntiles; t += B) {
+      const uint64_t base = t * kTile + threadIdx.x;
+      u32x4 y[U];
+      if ((t + 1) * kTile <= nfull) {
+        oneshot_reduce<C, R, U, true>(y, a, base, nfull);
+        store_tile<U, true, false>(dst, y, base, nfull);
+      } else {
+        oneshot_reduce<C, R, U, false>(y, a, base, nfull);
+        store_tile<U, false, false>(dst, y, base, nfull);
+      }
+    }
+  } else {
+    // Peers read this rank's input until they signal; their loads of a batch
+    // of tiles must be complete before this rank overwrites those tiles
+    // (write after read across ranks, no data handed over), so one barrier
+    // separates each batch's loads from its stores.  Every rank's slot runs
+    // the same number of batches.
+    constexpr int H = inplace_batch<U>();
+    for (uint64_t t0 = slot; t0 < ntiles; t0 += H * B) {
+      u32x4 y[H][U];
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const uint64_t t = t0 + h * B;
+        const uint64_t base = t * kTile + threadIdx.x;
+        if ((t + 1) * kTile <= nfull)
+          oneshot_reduce<C, R, U, true>(y[h], a, base, nfull);
+        else if (t < ntiles)
+          oneshot_reduce<C, R, U, false>(y[h], a, base, nfull);
+      }
+      chans.template barrier_all<Sync::kAfterReads>();
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const uint64_t t = t0 + h * B;
+        const uint64_t base = t * kTile + threadIdx.x;
+        if ((t + 1) * kTile <= nfull)
+          store_tile<U, true, false>(dst, y[h], base, nfull);
+        else if (t < ntiles)
+          store_tile<U, false, false>(dst, y[h], base, nfull);
+      }
+    }
   }
 
   if (ntail != 0 && slot == 0) {
     u32x4 y = {0u, 0u, 0u, 0u};
     if (threadIdx.x == 0) y = reduce_partial<C, R>(a, nfull, ntail);
-    if constexpr (kInPlace) chans.template barrier_all<true>();
+    if constexpr (kInPlace) chans.template barrier_all<Sync::kAfterReads>();
     if (threadIdx.x == 0) store_partial<C>(dst, nfull, y, ntail);
   }
 }
@@ -257,9 +295,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
       reduce_tile<C, R, U>(y, cur);
       store_tile<U, true, false>(mine, y, lane_base + t * kTile, v_full);  // re-read by the all-gather: cached
       if (!more) break;
-#pragma unroll
       for (int u = 0; u < U; ++u)
-#pragma unroll
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
       t = tn;
     }
@@ -282,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   // input, and in place rank r alone reads in[p][chunk r], earlier, in this
   // lane).  Publishing or acquiring memory here would only cost an L2
   // write-back and invalidate per workgroup.
-  chans.template barrier_all<false>();
+  chans.template barrier_all<Sync::kArrival>();
 
   // All-gather: put the reduced chunk into every peer's output, newest tiles
   // first (they are the likeliest to still be in cache), again pipelined one
@@ -348,7 +384,6 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
   const uint64_t nv = v_full - v_lo;
   const uint64_t nfull_tiles = nv / kTile;
   const bool owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(nfull_tiles % B);
-  const RankChannels chans{a.ch, R, rank, slot};
   const uint64_t lane_base = v_lo + threadIdx.x;
 
   if (static_cast<uint64_t>(slot) < nfull_tiles) {
@@ -364,9 +399,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
       reduce_tile<C, R, U>(y, cur);
       put_all_tile<C, R, U, true>(a, y, lane_base + t * kTile, v_full);
       if (!more) break;
-#pragma unroll
       for (int u = 0; u < U; ++u)
-#pragma unroll
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
       t = tn;
     }
@@ -506,7 +539,6 @@ __global__ __launch_bounds__(kThreads) void mscl_allgather_kernel(KernelArgs a) 
       if (more) allgather_load(nxt, src, tn * kTile + threadIdx.x, nv, (tn + 1) * kTile <= nv);
       allgather_store<R>(a, rank, skip_own, dst0, cur, t * kTile + threadIdx.x, nv, (t + 1) * kTile <= nv);
       if (!more) break;
-#pragma unroll
       for (int u = 0; u < kAllGatherU; ++u) cur[u] = nxt[u];
       t = tn;
     }
@@ -524,12 +556,13 @@ __global__ __launch_bounds__(kThreads) void mscl_allgather_kernel(KernelArgs a) 
 }
 
 // ----------------------------------------------------------------------------
-// Channel self-test: the pages' signal/wait contract checked directly.  Every
-// round, each (rank, slot) workgroup writes a 4 KiB mailbox, runs the ordered
-// barrier, reads the mailbox of the next rank's same slot (a workgroup on a
-// different XCD) and counts words that differ from what that peer wrote
-// before it signalled; a second ordered barrier keeps the peer from
-// overwriting its mailbox before the reads are done.
+// Channel self-test: the barriers' contracts checked directly.  Every round,
+// each (rank, slot) workgroup writes a 4 KiB mailbox, runs the publishing
+// barrier (the pages' signal/wait), reads the mailbox of the next rank's same
+// slot (a workgroup on a different XCD) and counts words that differ from
+// what that peer wrote before it signalled; then a write-after-read barrier
+// (Sync::kAfterReads) must keep the peer from overwriting its mailbox with
+// the next round's words before those reads are done.
 // ----------------------------------------------------------------------------
 
 constexpr int kSelftestWords = 1024;  // u32 words per mailbox (4 per lane)
@@ -559,13 +592,13 @@ __global__ __launch_bounds__(kThreads) void mscl_channel_selftest_kernel(KernelA
       const int i = j * kThreads + threadIdx.x;
       mine[i] = selftest_word(k, rank, slot, i);
     }
-    chans.template barrier_all<true>();
+    chans.template barrier_all<Sync::kPublish>();
 #pragma unroll
     for (int j = 0; j < kSelftestWords / kThreads; ++j) {
       const int i = j * kThreads + threadIdx.x;
       bad += theirs[i] != selftest_word(k, peer, slot, i);
     }
-    chans.template barrier_all<true>();
+    chans.template barrier_all<Sync::kAfterReads>();
   }
   if (bad) __hip_atomic_fetch_add(mismatches, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -218,8 +218,9 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
  *                   128 KiB (R <= 8), 64 KiB (R <= 16);
  *   fused two-shot  bytes <= 4 MiB;
  *   two-shot        above.
- * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: the
- * one-shot would need an ordered barrier on every tile.  Pure host
+ * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: in
+ * place the one-shot needs a barrier between loads and stores, the fused
+ * two-shot none.  Pure host
  * computation.  MSCL_ONESHOT_MAX_BYTES (environment, read once) replaces the
  * one-shot limit for every R.  mscl_channel_plan reports the in-place choice.
  * Errors: INVALID_ARGUMENT.
@@ -252,11 +253,14 @@ mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t channel, uint64_t w
  * Check the channel contract on the device (for tests and bring-up; it
  * synchronises and allocates, unlike the collectives).  For `rounds` rounds,
  * every (rank, slot) workgroup writes a 4 KiB mailbox, signals and waits on
- * the ordered barrier, reads the mailbox of the next rank's same slot (a
+ * the publishing barrier, reads the mailbox of the next rank's same slot (a
  * workgroup on another XCD for R > 1) and compares it with what that peer
  * wrote before signalling, since the pages' signal promises that every write
  * issued before it has completed (MSCCL++ README, Key Concepts, Channels);
- * then it runs a second barrier before the next round overwrites the mailbox.
+ * then a second, write-after-read barrier (the one the in-place one-shot
+ * uses) must hold the peer back from overwriting its mailbox with the next
+ * round's words until those reads are done; a word from the wrong round is
+ * a mismatch too.
  *   mismatches : receives the number of 32-bit words read that differed
  *                (0 when the channel keeps its promise).
  * Errors: INVALID_ARGUMENT, TIMEOUT (a wait ran out of time), HIP.
