@@ -56,7 +56,7 @@ TINY_COUNTS = (1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 1000,
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_tiny_brute_force(dtype):
     """R = 1..16, ragged lengths (every residue mod the vector width, n < R),
-    special values mixed in, both algorithms, out of place and in place."""
+    special values mixed in, every algorithm, out of place and in place."""
     g = np.random.default_rng(4242)
     specials = P.special_patterns(dtype)
     for R in range(1, 17):
@@ -146,8 +146,12 @@ def test_fp16_sweep():
 
 @pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused"])
 @pytest.mark.parametrize("R,n,dtype", [(8, 3 * 256 * 2 * 8 * 64 + 5, "bf16"), (16, 1_000_003, "bf16"),
-                                       (4, 777_777, "fp32"), (3, 1 << 20, "fp16"), (8, 9_437_185, "fp16")])
+                                       (4, 777_777, "fp32"), (3, 1 << 20, "fp16"), (8, 9_437_185, "fp16"),
+                                       (2, 3_000_001, "bf16")])
 def test_in_place(algo, R, n, dtype):
+    """In place at sizes where each one-shot workgroup runs several barrier
+    batches (4, 2 or 1 tiles per batch at U = 2, 4, 1), the last one partial,
+    with a ragged tail."""
     xs = P.rand_inputs(R, n, dtype, seed=n % 997)
     want = O.allreduce(xs, dtype)
     G.note(f"in place R={R} n={n} {dtype} {algo}")
