@@ -150,7 +150,7 @@ def test_fp16_sweep():
                                        (2, 3_000_001, "bf16")])
 def test_in_place(algo, R, n, dtype):
     """In place at sizes where each one-shot workgroup runs several barrier
-    batches (4, 2 or 1 tiles per batch at U = 2, 4, 1), the last one partial,
+    batches (8, 4 or 2 tiles per batch at U = 1, 2, 4), the last one partial,
     with a ragged tail."""
     xs = P.rand_inputs(R, n, dtype, seed=n % 997)
     want = O.allreduce(xs, dtype)
