@@ -459,19 +459,41 @@ __global__ __launch_bounds__(kThreads) void mscl_reduce_scatter_kernel(KernelArg
     const void* src[R];
 #pragma unroll
     for (int p = 0; p < R; ++p) src[p] = static_cast<const u32x4*>(a.in[p]) + src0;
-    for (uint64_t t = slot; t < ntiles; t += a.nblk) {
-      const uint64_t base = t * kTile + threadIdx.x;
+    // Full tiles, software pipelined as in the two-shot's reduce-scatter:
+    // the next tile's loads are issued before the current one is reduced
+    // and stored (R = 4 fp32, 128 MiB inputs: 125 -> 117 us).  Inputs are
+    // read once and stream past the caches; the block is stored cacheable
+    // (streaming stores measured slower: R = 8 bf16, 220 vs 215 us).  In
+    // place (outputs[r] is block r of inputs[r]) a lane stores only vectors
+    // it has already loaded.
+    const uint64_t B = a.nblk;
+    const uint64_t nfull_tiles = nv / kTile;
+    const uint64_t lane = threadIdx.x;
+    if (static_cast<uint64_t>(slot) < nfull_tiles) {
+      uint64_t t = slot;
+      u32x4 cur[U][R];
+      load_tile<R, U, true, true>(cur, src, t * kTile + lane, nv);
+      while (true) {
+        const uint64_t tn = t + B;
+        const bool more = tn < nfull_tiles;
+        u32x4 nxt[U][R];
+        if (more) load_tile<R, U, true, true>(nxt, src, tn * kTile + lane, nv);
+        u32x4 y[U];
+        reduce_tile<C, R, U>(y, cur);
+        store_tile<U, true, false>(dst, y, t * kTile + lane, nv);
+        if (!more) break;
+        for (int u = 0; u < U; ++u)
+          for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
+        t = tn;
+      }
+    }
+    if (nfull_tiles < ntiles && static_cast<uint64_t>(slot) == nfull_tiles % B) {  // the partial tile
       u32x4 x[U][R];
       u32x4 y[U];
-      if ((t + 1) * kTile <= nv) {
-        load_tile<R, U, true, true>(x, src, base, nv);  // read once: streaming
-        reduce_tile<C, R, U>(y, x);
-        store_tile<U, true, false>(dst, y, base, nv);
-      } else {
-        load_tile<R, U, false, true>(x, src, base, nv);
-        reduce_tile<C, R, U>(y, x);
-        store_tile<U, false, false>(dst, y, base, nv);
-      }
+      const uint64_t base = nfull_tiles * kTile + lane;
+      load_tile<R, U, false, true>(x, src, base, nv);
+      reduce_tile<C, R, U>(y, x);
+      store_tile<U, false, false>(dst, y, base, nv);
     }
   } else {
     using Bits = typename C::Bits;
