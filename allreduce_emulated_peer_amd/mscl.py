@@ -206,8 +206,10 @@ def channel_plan(handle: int, count: int, dtype: int, algo: int = ALGO_AUTO, in_
 def allreduce_tensors(inputs, outputs, algo: int = ALGO_AUTO, stream=None) -> None:
     """AllReduce over lists of equal-shape contiguous CUDA(HIP) tensors.
 
-    dtype comes from the tensors (float32 / float16 / bfloat16); the stream
-    defaults to torch's current stream on the tensors' device.
+    dtype comes from the tensors (float32 / float16 / bfloat16); the call
+    runs with the tensors' device current (the channel set is looked up per
+    device, so mscl_channel_create must have been called for that device and
+    rank count); the stream defaults to torch's current stream there.
     """
     import torch
 
@@ -215,13 +217,16 @@ def allreduce_tensors(inputs, outputs, algo: int = ALGO_AUTO, stream=None) -> No
     if len(inputs) != len(outputs) or not inputs:
         raise ValueError("need one output per input")
     t0 = inputs[0]
+    if not t0.is_cuda:
+        raise ValueError("tensors must be on a GPU")
     for t in list(inputs) + list(outputs):
         if t.dtype != t0.dtype or t.numel() != t0.numel() or not t.is_contiguous() or t.device != t0.device:
             raise ValueError("tensors must share dtype, size and device and be contiguous")
     if t0.dtype not in codes:
         raise ValueError(f"unsupported dtype {t0.dtype}")
-    if stream is None:
-        stream = torch.cuda.current_stream(t0.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    allreduce([t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], t0.numel(), codes[t0.dtype],
-              len(inputs), algo, handle)
+    with torch.cuda.device(t0.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(t0.device)
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        allreduce([t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], t0.numel(), codes[t0.dtype],
+                  len(inputs), algo, handle)

@@ -230,3 +230,15 @@ def test_plain_c_consumer_links_and_loads():
     r = subprocess.run([driver, "0", "2", "16", "0", "/nonexistent", "/nonexistent"], capture_output=True,
                        text=True, timeout=60)
     assert r.returncode == 1 and "bad R" in r.stderr
+
+
+def test_allreduce_tensors_rejects_bad_arguments_before_any_gpu_call():
+    import torch
+
+    cpu = [torch.zeros(8, dtype=torch.bfloat16) for _ in range(2)]
+    with pytest.raises(ValueError, match="one output per input"):
+        M.allreduce_tensors(cpu, cpu[:1])
+    with pytest.raises(ValueError, match="one output per input"):
+        M.allreduce_tensors([], [])
+    with pytest.raises(ValueError, match="on a GPU"):
+        M.allreduce_tensors(cpu, [torch.empty_like(t) for t in cpu])

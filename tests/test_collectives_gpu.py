@@ -147,3 +147,27 @@ def test_full_size_prefill_shape():
     M.allgather([t.data_ptr() for t in blocks], [t.data_ptr() for t in outs], rc, M.BFLOAT16, R, stream)
     torch.cuda.synchronize()
     G.assert_matches_oracle_on_device(outs, want, "bf16", "reduce_scatter + allgather")
+
+
+def test_allreduce_tensors_wrapper():
+    """The torch convenience wrapper: dtype from the tensors, torch's current
+    stream by default, an explicit stream, in place."""
+    R, n = 4, 50_001
+    w = W.custom(R, "bf16", n, "normal", seed_index=21)
+    xs = W.generate_all(w)
+    want = O.bits_of(O.allreduce(xs, "bf16"), "bf16")
+    G.channel(R)
+    ins = [G.to_device(x, "bf16") for x in xs]
+    outs = [G.poison_like(t) for t in ins]
+    G.note("allreduce_tensors R=4 bf16 default stream")
+    M.allreduce_tensors(ins, outs)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(G.to_host_bits(o, "bf16"), want)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    G.note("allreduce_tensors R=4 bf16 explicit stream, in place")
+    M.allreduce_tensors(ins, ins, algo=M.ALGO_TWO_SHOT, stream=s)
+    s.synchronize()
+    for t in ins:
+        assert np.array_equal(G.to_host_bits(t, "bf16"), want)
