@@ -254,8 +254,20 @@ def main() -> int:
         latency[f"graph_us_per_call_16KiB_{lw.name}"] = round(dev_us, 2)
         log(f"[bench] {lw.name}: p50 {p50:.2f} us per call (events), {dev_us:.2f} us per call replayed from a graph")
     if latency:
+        # latency floor: the smallest event p50 over the R = 8 bf16 sizes up to 64 KiB
+        floor = {}
+        for k in (10, 12, 14, 16):
+            fw = W.sweep_bf16(k)
+            fi = device_inputs(fw)
+            fo = [torch.empty_like(t) for t in fi]
+            floor[fw.bytes_per_rank] = p50_us(caller(fw, fi, fo), args.latency_iters)[0]
+            del fi, fo
+        best = min(floor, key=floor.get)
+        latency["floor_p50_us_le_64KiB_r8_bf16"] = round(floor[best], 2)
+        latency["floor_at_bytes"] = best
         latency["note"] = ("p50_us: HIP events around each call, host launch cost included; "
-                           "graph_us_per_call: 100 calls replayed from one graph (device time per call)")
+                           "graph_us_per_call: 100 calls replayed from one graph (device time per call); "
+                           "floor: smallest p50 over 1, 4, 16 and 64 KiB per rank")
     host = None
     if not args.main_only:
         # Host cost of one call (ctypes + validation + launch): CPU clock
@@ -489,7 +501,8 @@ def main() -> int:
             t_total += time.perf_counter() - t1
             reps += 1
         t_per = t_total / reps
-        cpu = {"value": round(n_sample * 2 / t_per / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        cpu = {"value": round(n_sample * 2 / t_per / 1e9, 3), "unit": "GB/s", "cores": cores,
+               "host_cpu_count": os.cpu_count(), "kind": "oracle",
                "sample": f"plain-C oracle, first {n_sample} elements of each of the 8 rank buffers of {w.name}, "
                          f"{reps} runs, {t_per * 1000:.1f} ms per run; same algbw accounting (S/t)"}
         log(f"[bench] cpu oracle: {cpu['value']} GB/s algbw on {cores} threads")
