@@ -136,8 +136,8 @@ struct RankChannels {
   // write-back and invalidate, 6-10 us per launch.
   template <Sync kSync>
   __device__ void barrier_all() const {
-    constexpr bool kOrdered = kSync == Sync::kPublish;
-    if (kOrdered) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's accesses, published
+    constexpr bool kPublishing = kSync == Sync::kPublish;
+    if (kPublishing) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's accesses, published
     if (kSync == Sync::kAfterReads) __builtin_amdgcn_s_waitcnt(0);  // this thread's accesses, completed
     __syncthreads();  // every local thread has reached the barrier
     if (threadIdx.x < 64) {
@@ -147,17 +147,17 @@ struct RankChannels {
       const uint32_t epoch = __hip_atomic_load(consumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
       const bool active = peer < nranks && peer != rank;
       if (active) {
-        if (kOrdered)
+        if (kPublishing)
           signal(peer);
         else
           signal_arrival(peer);
       }
       if (active) wait(peer, epoch);
-      if (kOrdered) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (kPublishing) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (peer == 0) __hip_atomic_store(consumed, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();  // the rest of the workgroup is now synchronised with the peers
-    if (kOrdered) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // and sees what they published
+    if (kPublishing) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // and sees what they published
   }
 };
 

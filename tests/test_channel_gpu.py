@@ -1,9 +1,12 @@
-"""The channel layer's ordering contract, checked on the device.
+"""The channel layer's ordering contracts, checked on the device.
 
 mscl_channel_selftest makes every (rank, slot) workgroup write a mailbox,
-signal/wait on the ordered barrier and read the next rank's mailbox, which a
-workgroup on another XCD wrote before it signalled.  Any stale word means the
-release/acquire pairing across the XCDs' separate L2 caches is broken.
+signal/wait on the publishing barrier and read the next rank's mailbox, which
+a workgroup on another XCD wrote before it signalled, then pass the
+write-after-read barrier before the next round overwrites the mailboxes.  A
+stale word means the release/acquire pairing across the XCDs' separate L2
+caches is broken; a word from the next round means a peer's store overtook
+this workgroup's loads across the write-after-read barrier.
 """
 
 import pytest
