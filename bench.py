@@ -187,7 +187,10 @@ def main() -> int:
     _hip.hipEventDestroy.argtypes = [_ct.c_void_p]
     HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
-    def p50_us_timing_events(call, iters):
+    def bracket_us(call, iters, before=None):
+        """Median time between timing-only HIP events recorded just before
+        and just after each call (`before`, if given, runs ahead of the
+        first event each time)."""
         def make():
             e = _ct.c_void_p()
             if _hip.hipEventCreateWithFlags(_ct.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
@@ -199,6 +202,8 @@ def main() -> int:
         s_ = _ct.c_void_p(stream.cuda_stream)
         torch.cuda.synchronize()
         for a, b in evs:
+            if before is not None:
+                before()
             _hip.hipEventRecord(a, s_)
             call()
             _hip.hipEventRecord(b, s_)
@@ -212,6 +217,9 @@ def main() -> int:
             _hip.hipEventDestroy(a)
             _hip.hipEventDestroy(b)
         return float(np.median(t))
+
+    def p50_us_timing_events(call, iters):
+        return bracket_us(call, iters)
 
     def graph_us(w, ins, outs, algo=M.ALGO_AUTO, reps=100):
         """Device time per call: `reps` calls captured in one HIP graph and
@@ -464,8 +472,8 @@ def main() -> int:
 
     if args.sweep:
         # Cold calls: a 768 MiB device copy (through the 256 MB Infinity Cache
-        # and every L2) runs before each call, and HIP events bracket the call
-        # alone.  The copy takes ~100 us, so the host is always ahead of the
+        # and every L2) runs before each call, and timing-only HIP events
+        # bracket the call alone.  The copy takes ~100 us, so the host is always ahead of the
         # GPU and the event interval is the call's device time.  Sizes from
         # 32 MiB per rank up are cold by construction (2RS >= 512 MiB).
         fl_src = torch.empty(768 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -473,15 +481,7 @@ def main() -> int:
 
         def cold_us(call, iters=15, flush_bytes=None):
             src, dst = (fl_src, fl_dst) if flush_bytes is None else (fl_src[:flush_bytes], fl_dst[:flush_bytes])
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-            torch.cuda.synchronize()
-            for a, b in ev:
-                dst.copy_(src)
-                a.record(stream)
-                call()
-                b.record(stream)
-            torch.cuda.synchronize()
-            return float(np.median([a.elapsed_time(b) * 1000.0 for a, b in ev]))
+            return bracket_us(call, iters, before=lambda: dst.copy_(src))
 
         algos = ((M.ALGO_ONE_SHOT, "one"), (M.ALGO_TWO_SHOT, "two"), (M.ALGO_TWO_SHOT_FUSED, "fused"))
         cw = W.sweep_bf16(10)
