@@ -185,6 +185,55 @@ def test_non_default_stream():
         G.assert_matches_oracle(outs, want, "bf16", f"side stream {algo}")
 
 
+def test_two_channel_sets_on_two_streams_concurrently():
+    """Channel sets of different rank counts are independent: an R = 4 fp32
+    and an R = 8 bf16 AllReduce (both with barriers: two-shot) issued
+    alternately on two streams, 20 calls each, may overlap on the device;
+    both results stay exact."""
+    wa = W.custom(4, "fp32", 3_000_017, "normal", seed_index=31)
+    wb = W.custom(8, "bf16", 4_000_037, "normal", seed_index=32)
+    xa, xb = W.generate_all(wa), W.generate_all(wb)
+    want_a, want_b = O.allreduce(xa, "fp32"), O.allreduce(xb, "bf16")
+    G.channel(4), G.channel(8)
+    ia, ib = [G.to_device(x, "fp32") for x in xa], [G.to_device(x, "bf16") for x in xb]
+    oa, ob = [G.poison_like(t) for t in ia], [G.poison_like(t) for t in ib]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    G.note("two channel sets, two streams, 20 two-shot calls each")
+    for _ in range(20):
+        M.allreduce([t.data_ptr() for t in ia], [t.data_ptr() for t in oa], wa.count, M.FLOAT32, 4,
+                    M.ALGO_TWO_SHOT, sa.cuda_stream)
+        M.allreduce([t.data_ptr() for t in ib], [t.data_ptr() for t in ob], wb.count, M.BFLOAT16, 8,
+                    M.ALGO_TWO_SHOT, sb.cuda_stream)
+    sa.synchronize()
+    sb.synchronize()
+    G.assert_matches_oracle(oa, want_a, "fp32", "R=4 on stream a")
+    G.assert_matches_oracle(ob, want_b, "bf16", "R=8 on stream b")
+    assert M.channel_check(G.channel(4)) == M.SUCCESS and M.channel_check(G.channel(8)) == M.SUCCESS
+
+
+def test_fp32_large_every_algorithm():
+    """fp32 at 32 MiB per rank, R = 8: 64 Ki sampled elements (and both ends)
+    against the oracle, and every algorithm bit-identical to the others on
+    every element."""
+    w = W.custom(8, "fp32", (32 << 20) // 4 + 3, "normal", seed_index=33)
+    xs = W.generate_all(w)
+    idx = G.sample_indices(w.count, seed=33)
+    want = O.allreduce_elements(xs, "fp32", idx)
+    dev_in = [G.to_device(x, "fp32") for x in xs]
+    res = {}
+    for algo in G.EXPLICIT:
+        G.note(f"fp32 R=8 32 MiB {algo}")
+        res[algo] = G.run(xs, "fp32", algo, dev_inputs=dev_in)
+        G.assert_outputs_equal_each_other(res[algo])
+        got = G.to_host_bits(res[algo][0], "fp32")[idx]
+        assert np.array_equal(got, want.view(np.uint32)), f"fp32 {algo}: sampled mismatch"
+    for r in range(8):
+        for algo in ("two_shot", "two_shot_fused"):
+            assert torch.equal(res["one_shot"][r].view(torch.uint8), res[algo][r].view(torch.uint8))
+
+
 def test_repeated_calls_keep_epochs():
     """10^4 back-to-back barrier launches: every semaphore epoch must line up
     (a mismatch would time out and be reported, or give wrong data)."""
