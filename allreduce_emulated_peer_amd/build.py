@@ -22,11 +22,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# the port channel's proxy drives the SDMA engines through HSA
+LIBS = ["-L/opt/rocm/lib", "-lhsa-runtime64"]
 
 
 def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp"
-    cmd = ["/opt/rocm/bin/hipcc", *FLAGS, *extra, "-o", tmp, SRC]
+    cmd = ["/opt/rocm/bin/hipcc", *FLAGS, *extra, "-o", tmp, SRC, *LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -53,6 +53,7 @@
 #include "../../include/mscl.h"
 #include "channel.hpp"
 #include "codec.hpp"
+#include "port.hpp"
 
 namespace mscl {
 
@@ -81,6 +82,7 @@ struct KernelArgs {
   uint32_t xcd_grouped;  // one-shot: all ranks of a slot on one XCD (needs nblk % 8 == 0)
   uint32_t in_place_mask;  // allgather: bit r set when rank r's input already is its own output block
   ChannelArgs ch;
+  PortArgs port;  // two-shot over a port channel only
 };
 
 // binary32 sum of one 16-byte vector position over the R ranks, in rank
@@ -253,63 +255,90 @@ __device__ inline void ag_load(u32x4 (&y)[U], const void* mine, uint64_t base, u
   }
 }
 
-template <class C, int R>
-__global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
+// Rank `rank`'s two-shot chunk, seen from one slot: elements [lo, hi), its
+// full 16-byte vectors [v_lo, v_full), the partial vector's element count,
+// and the slot's tiles t = slot, slot + B, ...: tiles below `nfull_tiles` lie
+// wholly inside the chunk; at most one partial tile (index nfull_tiles)
+// follows.
+struct Chunk {
+  uint64_t lo, hi, v_lo, v_full, nfull_tiles;
+  int ntail;  // nonzero only for the non-empty chunk that holds the buffer's end
+  bool owns_partial_tile;
+};
+
+template <class C, int U>
+__device__ inline Chunk chunk_of(const KernelArgs& a, int rank, int slot) {
   constexpr int V = C::V;
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  Chunk g;
+  g.lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, a.count);
+  g.hi = std::min<uint64_t>(g.lo + a.chunk, a.count);
+  g.v_lo = g.lo / V;  // chunk starts are multiples of V
+  g.v_full = g.hi / V;
+  g.ntail = g.hi > g.lo ? static_cast<int>(g.hi % V) : 0;
+  const uint64_t nv = g.v_full - g.v_lo;
+  g.nfull_tiles = nv / kTile;
+  g.owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(g.nfull_tiles % a.nblk);
+  return g;
+}
+
+// Reduce-scatter: chunk `rank` of every input -> own output `mine`.
+// Software pipelined: the loads of the slot's next tile are issued before
+// the current tile is reduced and stored, so each wave keeps R*U 16-byte
+// loads in flight while it computes.
+template <class C, int R>
+__device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& g, int slot, void* mine,
+                                              uint64_t lane_base) {
   constexpr int U = unroll_for<R>();
   constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
-  const int rank = blockIdx.x % R;
-  const int slot = blockIdx.x / R;
   const uint64_t B = a.nblk;
-  const uint64_t n = a.count;
-  const uint64_t lo = std::min<uint64_t>(static_cast<uint64_t>(rank) * a.chunk, n);
-  const uint64_t hi = std::min<uint64_t>(lo + a.chunk, n);
-  const uint64_t v_lo = lo / V;    // chunk starts are multiples of V
-  const uint64_t v_full = hi / V;  // end of the chunk's full vectors
-  // nonzero only for the non-empty chunk that holds the buffer's end
-  const int ntail = hi > lo ? static_cast<int>(hi % V) : 0;
-  const uint64_t nv = v_full - v_lo;
-  // Tiles t = slot, slot + B, ... belong to this slot.  Tiles below
-  // `nfull_tiles` lie wholly inside the chunk; at most one partial tile
-  // (index nfull_tiles) follows.
-  const uint64_t nfull_tiles = nv / kTile;
-  const bool owns_partial_tile = (nv % kTile) != 0 && slot == static_cast<int>(nfull_tiles % B);
-  const RankChannels chans{a.ch, R, rank, slot};
-  void* const mine = a.out[rank];
-  const uint64_t lane_base = v_lo + threadIdx.x;
-
-  // Reduce-scatter: chunk `rank` of every input -> own output.  Software
-  // pipelined: the loads of the slot's next tile are issued before the
-  // current tile is reduced and stored, so each wave keeps R*U 16-byte
-  // loads in flight while it computes.
-  if (static_cast<uint64_t>(slot) < nfull_tiles) {
+  if (static_cast<uint64_t>(slot) < g.nfull_tiles) {
     uint64_t t = slot;
     u32x4 cur[U][R];
-    load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * kTile, v_full);
+    load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * kTile, g.v_full);
     while (true) {
       const uint64_t tn = t + B;
-      const bool more = tn < nfull_tiles;
+      const bool more = tn < g.nfull_tiles;
       u32x4 nxt[U][R];
-      if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, v_full);
+      if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, g.v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
-      store_tile<U, true, false>(mine, y, lane_base + t * kTile, v_full);  // re-read by the all-gather: cached
+      store_tile<U, true, false>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather: cached
       if (!more) break;
       for (int u = 0; u < U; ++u)
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
       t = tn;
     }
   }
-  if (owns_partial_tile) {
+  if (g.owns_partial_tile) {
     u32x4 x[U][R];
     u32x4 y[U];
-    const uint64_t base = lane_base + nfull_tiles * kTile;
-    load_tile<R, U, false, kStreamRsLoads>(x, a.in, base, v_full);
+    const uint64_t base = lane_base + g.nfull_tiles * kTile;
+    load_tile<R, U, false, kStreamRsLoads>(x, a.in, base, g.v_full);
     reduce_tile<C, R, U>(y, x);
-    store_tile<U, false, false>(mine, y, base, v_full);
+    store_tile<U, false, false>(mine, y, base, g.v_full);
   }
+  if (g.ntail != 0 && slot == 0 && threadIdx.x == 0)
+    store_partial<C>(mine, g.v_full, reduce_partial<C, R>(a, g.v_full, g.ntail), g.ntail);
+}
+
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t B = a.nblk;
+  const Chunk g = chunk_of<C, U>(a, rank, slot);
+  const uint64_t v_full = g.v_full, nfull_tiles = g.nfull_tiles;
+  const int ntail = g.ntail;
+  const bool owns_partial_tile = g.owns_partial_tile;
+  const RankChannels chans{a.ch, R, rank, slot};
+  void* const mine = a.out[rank];
+  const uint64_t lane_base = g.v_lo + threadIdx.x;
+
+  twoshot_reduce_scatter<C, R>(a, g, slot, mine, lane_base);
   const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
-  if (tail_owner) store_partial<C>(mine, v_full, reduce_partial<C, R>(a, v_full, ntail), ntail);
 
   // signal / wait with the same slot of every peer rank.  Arrival only: no
   // data crosses ranks here.  The all-gather below reads only vectors this
@@ -349,6 +378,51 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       t = tn;
     }
+  }
+}
+
+// Two-shot over a port channel: the reduce-scatter runs here, as in the
+// two-shot; the all-gather puts go to the host proxy, which copies each rank's
+// reduced chunk into the R-1 peer outputs with DMA engines.  Every workgroup
+// publishes its part of the chunk to memory at system scope (the copy engines
+// read memory, not this XCD's L2) and counts itself in; the rank's last
+// workgroup posts the R-1 puts, one lane per peer, and its first lane waits
+// until the proxy reports them done, so the call ends on the stream only once
+// every output is complete.  In place, rank r's puts overwrite in[p][chunk r],
+// which only rank r read, before its workgroups counted in.
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot_port(KernelArgs a) {
+  constexpr int U = unroll_for<R>();
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const Chunk g = chunk_of<C, U>(a, rank, slot);
+  char* const mine = static_cast<char*>(a.out[rank]);
+  twoshot_reduce_scatter<C, R>(a, g, slot, mine, g.v_lo + threadIdx.x);
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // this thread's stores, published at system scope
+  __syncthreads();
+  __shared__ bool last;
+  if (threadIdx.x == 0) {
+    const uint32_t prior =
+        __hip_atomic_fetch_add(a.port.arrived + rank, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = prior + 1 == a.nblk;
+    if (last) __hip_atomic_store(a.port.arrived + rank, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last || threadIdx.x >= 64) return;
+
+  const PortChannel port{a.port, a.ch};
+  const uint64_t off = g.lo * C::kElemBytes;
+  const uint64_t bytes = (g.hi - g.lo) * C::kElemBytes;
+  if (bytes == 0) return;
+  const int peer = threadIdx.x;
+  if (peer < R && peer != rank && rank != a.ch.drop_rank)
+    port.put(rank, static_cast<char*>(a.out[peer]) + off, mine + off, bytes);
+  if (threadIdx.x == 0) {
+    const uint32_t target = __hip_atomic_load(a.port.issued + rank, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                            static_cast<uint32_t>(R - 1);
+    __hip_atomic_store(a.port.issued + rank, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    port.flush(rank, target);
   }
 }
 
@@ -638,7 +712,8 @@ enum {
   kReduceScatterVec = 4,
   kReduceScatterElem = 5,
   kAllGatherVec = 6,
-  kAllGatherElem = 7
+  kAllGatherElem = 7,
+  kAlgoTwoShotPort = 8
 };
 
 template <class C, int R>
@@ -652,6 +727,7 @@ constexpr KernelFn kernel_for(int kind) {
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
     case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;
     case kAllGatherElem: return &mscl_allgather_kernel<C, R, false>;
+    case kAlgoTwoShotPort: return &mscl_twoshot_port<C, R>;
   }
   return nullptr;
 }

@@ -57,9 +57,14 @@ typedef enum {
   MSCL_ALGO_AUTO = 0,          /* by size: one-shot, then fused two-shot, then two-shot */
   MSCL_ALGO_ONE_SHOT = 1,      /* every rank reads all R inputs and writes its own output */
   MSCL_ALGO_TWO_SHOT = 2,      /* reduce-scatter, device signal/wait barrier, all-gather put */
-  MSCL_ALGO_TWO_SHOT_FUSED = 3 /* reduce-scatter whose all-gather put goes out from registers
-                                  (no re-read of the reduced chunk, no barrier inside the call;
-                                  completion is the end of the call on the stream) */
+  MSCL_ALGO_TWO_SHOT_FUSED = 3, /* reduce-scatter whose all-gather put goes out from registers
+                                   (no re-read of the reduced chunk, no barrier inside the call;
+                                   completion is the end of the call on the stream) */
+  MSCL_ALGO_TWO_SHOT_PORT = 4   /* reduce-scatter in the kernel; the all-gather puts go through a
+                                   port channel: each rank's last workgroup posts R-1 put
+                                   requests to a host proxy thread, which copies them with the
+                                   SDMA engines, and waits for their completion.  Never chosen
+                                   by AUTO (see mscl_allreduce) */
 } mscl_algo_t;
 
 typedef int mscl_status_t;
@@ -151,8 +156,8 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  *   dtype   : element type of inputs and outputs.
  *   nranks  : R, 1..MSCL_MAX_RANKS; a channel set for (current device, R)
  *             must exist (mscl_channel_create).
- *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT, _TWO_SHOT or _TWO_SHOT_FUSED.  All
- *             give bit-identical results.
+ *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT, _TWO_SHOT, _TWO_SHOT_FUSED or
+ *             _TWO_SHOT_PORT.  All give bit-identical results.
  *   stream  : hipStream_t on the current device (NULL = default stream).
  * Every pointer must be 16-byte aligned and on the current device.  The call
  * is asynchronous: it validates, launches one kernel on `stream` and
@@ -161,6 +166,18 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * pointer tables travel in the kernel arguments.
  * A TIMEOUT recorded by an earlier call makes this call return TIMEOUT
  * without launching, until mscl_channel_reset().
+ * MSCL_ALGO_TWO_SHOT_PORT follows the pages' PortChannel (MSCCL++ README, Key
+ * Concepts, "PortChannel and MemoryChannel", "Host-Side Communication
+ * Proxy"): GPU threads only post requests, and a CPU proxy moves the data
+ * with DMA engines.  The first such call on a channel set allocates the
+ * request ring (host-mapped memory) and completion counters and starts the
+ * proxy thread, once; later calls allocate nothing.  The kernel ends only
+ * after the proxy has completed every put, so stream order still marks the
+ * result as ready; if the proxy does not finish within the wait bound the
+ * channel records TIMEOUT.  The proxy checks every request against the
+ * device allocations before copying and records INVALID_ARGUMENT for one
+ * that leaves them.  Each put costs the copy engines ~20 us of set-up, so
+ * this algorithm is for moving data without compute units, not for speed.
  * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
  */
 mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], size_t count,
@@ -168,8 +185,8 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
 
 /*
  * ReduceScatter (sum) over R emulated ranks — the two-shot's first half as a
- * standard collective (the pages' library implements the standard
- * collective API: MSCCL++ ASPLOS'26 abstract).
+ * standard collective (the pages' library offers the usual collective
+ * interface: MSCCL++ ASPLOS'26 abstract).
  *   inputs    : host array of nranks device pointers; inputs[p] holds
  *               nranks * recvcount elements.  Read only; may alias each other.
  *   outputs   : host array of nranks device pointers; outputs[r] receives

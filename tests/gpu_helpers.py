@@ -20,8 +20,8 @@ from oracle import allreduce as O
 TORCH_DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 CODES = {"fp32": M.FLOAT32, "fp16": M.FLOAT16, "bf16": M.BFLOAT16}
 ALGOS = {"one_shot": M.ALGO_ONE_SHOT, "two_shot": M.ALGO_TWO_SHOT, "two_shot_fused": M.ALGO_TWO_SHOT_FUSED,
-         "auto": M.ALGO_AUTO}
-EXPLICIT = ("one_shot", "two_shot", "two_shot_fused")
+         "two_shot_port": M.ALGO_TWO_SHOT_PORT, "auto": M.ALGO_AUTO}
+EXPLICIT = ("one_shot", "two_shot", "two_shot_fused", "two_shot_port")
 POISON = 0xA5
 
 _channels = {}

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 DRIVER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_driver")
 CODES = {"fp32": 0, "fp16": 1, "bf16": 2}
-ALGOS = {"auto": 0, "one_shot": 1, "two_shot": 2, "two_shot_fused": 3}
+ALGOS = {"auto": 0, "one_shot": 1, "two_shot": 2, "two_shot_fused": 3, "two_shot_port": 4}
 STORAGE = {"fp32": np.uint32, "fp16": np.uint16, "bf16": np.uint16}
 
 CASES = [
@@ -26,6 +26,7 @@ CASES = [
     (16, "bf16", 1_000_003, "normal", "two_shot", False),
     (3, "fp16", 77_777, "uniform", "two_shot_fused", False),
     (8, "bf16", 262_147, "normal", "two_shot", True),
+    (5, "bf16", 300_001, "normal", "two_shot_port", False),
 ]
 
 

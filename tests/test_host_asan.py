@@ -26,7 +26,8 @@ def test_host_code_is_asan_clean(tmp_path):
     common = ["-I", os.path.join(ROOT, "include"), "-O1", "-g", "-fno-omit-frame-pointer",
               "-Xarch_host", "-fsanitize=address"]
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
-                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *common, "-o", str(lib), src],
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *common, "-o", str(lib), src,
+                    "-L/opt/rocm/lib", "-lhsa-runtime64"],
                    check=True, capture_output=True)
     subprocess.run([CLANG, *common, "-o", str(exe), os.path.join(HERE, "host_asan_driver.c"),
                     str(lib), f"-Wl,-rpath,{tmp_path}"], check=True, capture_output=True)

@@ -29,7 +29,7 @@ def gpu():
     yield
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "auto"])
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "two_shot_port", "auto"])
 def test_integer_workload_exact(algo):
     w = W.integer_small()
     xs = W.generate_all(w)
@@ -41,7 +41,7 @@ def test_integer_workload_exact(algo):
     G.assert_matches_oracle(outs, O.allreduce(xs, "fp32"), "fp32", w.name)
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "auto"])
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "two_shot_port", "auto"])
 def test_decode_bf16(algo):
     w = W.decode_bf16()
     xs = W.generate_all(w)
@@ -91,7 +91,7 @@ def test_hand_cases_on_gpu():
                 assert np.all(got == int(want, 16)), f"{dtype} {ins} {algo}: {hex(int(got[0]))} != {want}"
 
 
-@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused"])
+@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused", "two_shot_port"])
 def test_prefill_bf16_full(algo):
     w = W.prefill_bf16()
     xs = W.generate_all(w)
@@ -101,7 +101,7 @@ def test_prefill_bf16_full(algo):
     G.assert_matches_oracle_on_device(outs, want, "bf16", w.name)
 
 
-@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused"])
+@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused", "two_shot_port"])
 def test_ragged_outliers_full(algo):
     w = W.ragged_outliers_bf16()
     xs = W.generate_all(w)
@@ -138,13 +138,13 @@ def test_fp16_sweep():
                 got = G.to_host_bits(outs[0], "fp16")[idx]
                 assert np.array_equal(got, want.view(np.uint16)), f"{w.name} {algo}: sampled mismatch"
             for r in range(8):
-                for algo in ("two_shot", "two_shot_fused"):
+                for algo in ("two_shot", "two_shot_fused", "two_shot_port"):
                     assert torch.equal(res["one_shot"][r].view(torch.uint8), res[algo][r].view(torch.uint8))
         del dev_in, res
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused"])
+@pytest.mark.parametrize("algo", ["one_shot", "two_shot", "two_shot_fused", "two_shot_port"])
 @pytest.mark.parametrize("R,n,dtype", [(8, 3 * 256 * 2 * 8 * 64 + 5, "bf16"), (16, 1_000_003, "bf16"),
                                        (4, 777_777, "fp32"), (3, 1 << 20, "fp16"), (8, 9_437_185, "fp16"),
                                        (2, 3_000_001, "bf16")])
@@ -230,7 +230,7 @@ def test_fp32_large_every_algorithm():
         got = G.to_host_bits(res[algo][0], "fp32")[idx]
         assert np.array_equal(got, want.view(np.uint32)), f"fp32 {algo}: sampled mismatch"
     for r in range(8):
-        for algo in ("two_shot", "two_shot_fused"):
+        for algo in ("two_shot", "two_shot_fused", "two_shot_port"):
             assert torch.equal(res["one_shot"][r].view(torch.uint8), res[algo][r].view(torch.uint8))
 
 
@@ -244,9 +244,9 @@ def test_repeated_calls_keep_epochs():
     outs = [G.poison_like(t) for t in ins]
     h = G.channel(R)
     stream = torch.cuda.current_stream().cuda_stream
-    G.note("10^4 repeated one-shot / two-shot / fused two-shot calls")
+    G.note("10^4 repeated one-shot / two-shot / fused two-shot / port two-shot calls")
     for i in range(10_000):
-        algo = (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED)[i % 3]
+        algo = (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT)[i % 4]
         M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, algo, stream)
         if i % 1000 == 999:
             torch.cuda.synchronize()
@@ -272,7 +272,7 @@ def test_graph_capture_and_replay():
     want = O.allreduce(xs, "bf16")
     ins = [G.to_device(x, "bf16") for x in xs]
     G.channel(R)
-    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_FUSED):
+    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT):
         outs = [G.poison_like(t) for t in ins]
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -303,13 +303,15 @@ def test_graph_capture_and_replay():
         del g
 
 
-@pytest.mark.parametrize("algo,in_place", [(M.ALGO_TWO_SHOT, False), (M.ALGO_ONE_SHOT, True)])
+@pytest.mark.parametrize("algo,in_place", [(M.ALGO_TWO_SHOT, False), (M.ALGO_ONE_SHOT, True),
+                                           (M.ALGO_TWO_SHOT_PORT, False)])
 def test_timeout_is_reported_not_hung(algo, in_place):
-    """Force a missing signal from the host (rank 1 skips signal()) with a
-    2 ms bound on every wait(): the kernel must exit, the status must read
-    TIMEOUT, further calls must refuse until reset, and a reset must bring
-    the channel back.  Both barrier kinds: the two-shot's arrival-only one and
-    the in-place one-shot's ordered one."""
+    """Force a missing signal from the host (rank 1 skips signal(), or with
+    the port channel posts no puts) with a 2 ms bound on every wait(): the
+    kernel must exit, the status must read TIMEOUT, further calls must refuse
+    until reset, and a reset must bring the channel back.  The two-shot's
+    arrival-only barrier, the in-place one-shot's after-reads barrier, and
+    the port channel's wait for the proxy."""
     R, n = 4, 100_000
     xs = P.rand_inputs(R, n, "fp32", seed=31)
     want = O.allreduce(xs, "fp32")
@@ -330,7 +332,8 @@ def test_timeout_is_reported_not_hung(algo, in_place):
         M.channel_set_fault_controls(h, 0, -1)
         M.channel_reset(h)
     assert M.channel_check(h) == M.SUCCESS
-    outs = G.run(xs, "fp32", {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_ONE_SHOT: "one_shot"}[algo], in_place=in_place)
+    names = {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_ONE_SHOT: "one_shot", M.ALGO_TWO_SHOT_PORT: "two_shot_port"}
+    outs = G.run(xs, "fp32", names[algo], in_place=in_place)
     G.assert_matches_oracle(outs, want, "fp32", "after reset")
 
 
@@ -382,5 +385,7 @@ def test_plan_geometry():
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 1
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
     assert q.uses_barrier == 0
+    q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_PORT)
+    assert q.algo == M.ALGO_TWO_SHOT_PORT and q.uses_barrier == 0 and q.chunk_elems == p.chunk_elems
     r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
     assert r16.chunk_elems % 8 == 0 and r16.chunk_elems * 16 >= W.ragged_outliers_bf16().count
