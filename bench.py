@@ -419,6 +419,33 @@ def main() -> int:
         del ri, ro
         torch.cuda.empty_cache()
 
+    port = None
+    if not args.main_only:
+        # The port channel (all-gather puts done by the host proxy on the SDMA
+        # engines) against the memory-channel two-shot, R = 8 bf16, device time
+        # per call between timing-only events.  The first call on a channel set
+        # starts the proxy and the engines; it is timed apart.
+        port = {"note": "us per call between timing-only HIP events, R=8 bf16; first_call_ms: proxy and SDMA "
+                        "engine start-up, once per channel set"}
+        for k in (19, 24, 27):  # 512 KiB, 16 MiB, 128 MiB per rank
+            pw = W.sweep_bf16(k)
+            pi = device_inputs(pw)
+            po = [torch.empty_like(t) for t in pi]
+            cp = caller(pw, pi, po, M.ALGO_TWO_SHOT_PORT)
+            if "first_call_ms" not in port:
+                t1 = time.perf_counter()
+                cp()
+                torch.cuda.synchronize()
+                port["first_call_ms"] = round((time.perf_counter() - t1) * 1000.0, 1)
+            iters = 50 if pw.bytes_per_rank <= (16 << 20) else 15
+            t_port = bracket_us(cp, iters)
+            t_two = bracket_us(caller(pw, pi, po, M.ALGO_TWO_SHOT), iters)
+            port[f"{pw.bytes_per_rank}B"] = {"port_us": round(t_port, 1), "two_shot_us": round(t_two, 1),
+                                            "port_algbw_GBps": round(pw.bytes_per_rank / t_port / 1e3, 1)}
+            log(f"[bench] port channel {pw.bytes_per_rank} B: {t_port:.1f} us (two-shot {t_two:.1f} us)")
+            del pi, po
+            torch.cuda.empty_cache()
+
     collectives = None
     if not args.main_only:
         # ReduceScatter of the prefill buffers (16 MiB blocks) and AllGather of
@@ -566,6 +593,7 @@ def main() -> int:
         "host_api": host,
         "decode_512KiB": decode,
         "ragged_r16": ragged,
+        "port_channel": port,
         "collectives": collectives,
     }
     print(json.dumps(line), flush=True)
