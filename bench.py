@@ -43,7 +43,7 @@ METRIC = "AllReduce algbw GB/s + % of HBM peak, R=8 bf16, 512KB–128MB; p50 µs
 HBM_PEAK_GBPS = 8000.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "twoshot_bf16_r8_128MiB_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "allreduce_emulated_peer_amd", "csrc", f)
-                  for f in ("kernels.hpp", "channel.hpp", "codec.hpp")]
+                  for f in ("kernels.hpp", "channel.hpp", "codec.hpp", "port.hpp")]
 
 
 def log(msg: str) -> None:
