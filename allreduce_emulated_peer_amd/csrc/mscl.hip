@@ -492,6 +492,16 @@ struct Bound {
   int drop_rank = -1;
 };
 
+// SUCCESS, or the failure an earlier call recorded in the set's status word
+// (a wait that timed out, or a port-channel request the proxy refused or
+// could not issue), which stands until mscl_channel_reset.
+mscl_status_t recorded_failure(const mscl_channel_s* ch) {
+  const int s = __atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE);
+  if (s == MSCL_SUCCESS) return MSCL_SUCCESS;
+  return fail(static_cast<mscl_status_t>(s), std::string("an earlier call on this channel set failed (") +
+                                                 mscl_status_string(s) + "); call mscl_channel_reset");
+}
+
 mscl_status_t bind_channel(int nranks, Bound* b) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
@@ -505,9 +515,7 @@ mscl_status_t bind_channel(int nranks, Bound* b) {
     b->timeout_us = b->ch->wait_timeout_us ? b->ch->wait_timeout_us : config().wait_timeout_us;
     b->drop_rank = b->ch->drop_rank;
   }
-  if (__atomic_load_n(b->ch->status_host, __ATOMIC_ACQUIRE) != MSCL_SUCCESS)
-    return fail(MSCL_ERR_TIMEOUT, "an earlier call timed out; call mscl_channel_reset");
-  return MSCL_SUCCESS;
+  return recorded_failure(b->ch);
 }
 
 void fill_args(KernelArgs* a, const Bound& b, const void* const inputs[], void* const outputs[], int nranks,
@@ -741,9 +749,7 @@ mscl_status_t mscl_channel_destroy(mscl_channel_t ch) {
 mscl_status_t mscl_channel_check(mscl_channel_t ch) {
   std::lock_guard<std::mutex> lock(g_mutex);
   if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
-  const int s = __atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE);
-  if (s != MSCL_SUCCESS) return fail(s, "a device-side wait timed out in an earlier call");
-  return MSCL_SUCCESS;
+  return recorded_failure(ch);
 }
 
 mscl_status_t mscl_channel_reset(mscl_channel_t ch) {
@@ -863,8 +869,7 @@ mscl_status_t mscl_channel_selftest(mscl_channel_t ch, uint32_t rounds, uint64_t
     b.timeout_us = ch->wait_timeout_us ? ch->wait_timeout_us : config().wait_timeout_us;
     b.drop_rank = ch->drop_rank;
   }
-  if (__atomic_load_n(ch->status_host, __ATOMIC_ACQUIRE) != MSCL_SUCCESS)
-    return fail(MSCL_ERR_TIMEOUT, "an earlier call timed out; call mscl_channel_reset");
+  if (const mscl_status_t st = recorded_failure(ch); st != MSCL_SUCCESS) return st;
   if (rounds == 0) return MSCL_SUCCESS;
   const int R = ch->nranks;
   KernelArgs a;

@@ -120,24 +120,31 @@ const char* mscl_last_error_string(void);
 mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out);
 
 /*
- * Drop one reference; the state is freed when the count reaches zero.  The
- * caller must have synchronised every stream that used the set.
+ * Drop one reference; the state is freed when the count reaches zero (the
+ * port channel's proxy thread, if one was started, is stopped and joined
+ * first).  The caller must have synchronised every stream that used the set;
+ * graphs captured with calls on it must not be replayed afterwards.
  * Errors: INVALID_ARGUMENT (null or unknown handle), HIP.
  */
 mscl_status_t mscl_channel_destroy(mscl_channel_t channel);
 
 /*
- * Report a device-side failure recorded by an earlier call on this set
- * (currently only a wait() timeout).  Reads the host-mapped status word; it
- * does not synchronise, so synchronise the stream first for a complete
- * answer.  Returns SUCCESS or the recorded code (TIMEOUT).
+ * Report a failure recorded by an earlier call on this set: a wait() that
+ * ran out of time (TIMEOUT), or a port-channel request the proxy refused
+ * (INVALID_ARGUMENT: a range outside the device allocations) or could not
+ * issue (HIP).  Reads the host-mapped status word; it does not synchronise,
+ * so synchronise the stream first for a complete answer.  Returns SUCCESS or
+ * the recorded code.
  */
 mscl_status_t mscl_channel_check(mscl_channel_t channel);
 
 /*
  * Zero the semaphores, the consumed-signal counters and the status word
  * (synchronous; the device must be idle on this set).  Needed after a
- * TIMEOUT, whose missing signals leave the counters out of step.
+ * TIMEOUT, whose missing signals leave the counters out of step.  A port
+ * channel keeps its allocations (graphs captured earlier still point at
+ * them): its proxy is stopped, its ring and counters zeroed, and the proxy
+ * started again.
  * Errors: INVALID_ARGUMENT, HIP.
  */
 mscl_status_t mscl_channel_reset(mscl_channel_t channel);
@@ -164,8 +171,8 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * returns.  The caller owns all buffers and keeps them alive until the stream
  * has finished.  Nothing is allocated or copied to the device per call: the
  * pointer tables travel in the kernel arguments.
- * A TIMEOUT recorded by an earlier call makes this call return TIMEOUT
- * without launching, until mscl_channel_reset().
+ * A failure recorded by an earlier call (see mscl_channel_check) makes this
+ * call return that code without launching, until mscl_channel_reset().
  * MSCL_ALGO_TWO_SHOT_PORT follows the pages' PortChannel (MSCCL++ README, Key
  * Concepts, "PortChannel and MemoryChannel", "Host-Side Communication
  * Proxy"): GPU threads only post requests, and a CPU proxy moves the data
