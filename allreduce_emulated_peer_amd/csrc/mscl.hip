@@ -156,7 +156,11 @@ void proxy_loop(PortState* ps, int* status_host) {
   std::vector<hsa_signal_t> pool;
   uint64_t tail = 0;
   uint64_t next_engine = 0;
-  int idle = 0;
+  // Poll without sleeping for 2 ms after the last request or completion (a
+  // sleep, with the kernel's timer slack, costs tens of microseconds per
+  // call); after that, back off to short sleeps so an idle set costs no core.
+  using Clock = std::chrono::steady_clock;
+  Clock::time_point last_activity = Clock::now();
   auto fail_status = [&](mscl_status_t s) { __atomic_store_n(status_host, static_cast<int>(s), __ATOMIC_RELEASE); };
   while (!ps->stop.load(std::memory_order_acquire)) {
     bool progress = false;
@@ -202,11 +206,10 @@ void proxy_loop(PortState* ps, int* status_host) {
       inflight.pop_back();
       progress = true;
     }
-    if (progress) {
-      idle = 0;
-    } else if (++idle > 4096) {
-      std::this_thread::sleep_for(std::chrono::microseconds(20));  // idle: stop spinning a core
-    }
+    if (progress)
+      last_activity = Clock::now();
+    else if (Clock::now() - last_activity > std::chrono::milliseconds(2))
+      std::this_thread::sleep_for(std::chrono::microseconds(20));
   }
   for (auto& f : inflight) {
     hsa_signal_wait_scacquire(f.sig, HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX, HSA_WAIT_STATE_BLOCKED);
