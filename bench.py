@@ -261,18 +261,34 @@ def main() -> int:
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Per-step kernel time from timing-only HIP events (no system-scope cache
+    # write-back at each record), on the stream the kernel runs on.
+    def timing_event():
+        e = _ct.c_void_p()
+        if _hip.hipEventCreateWithFlags(_ct.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+    ev = [(timing_event(), timing_event()) for _ in range(args.steps)]
+    s_main = _ct.c_void_p(stream.cuda_stream)
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in ev:
-        a.record(stream)
+        _hip.hipEventRecord(a, s_main)
         call()
-        b.record(stream)
+        _hip.hipEventRecord(b, s_main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1000.0 / args.steps
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    kern = []
+    for a, b in ev:
+        ms = _ct.c_float()
+        if _hip.hipEventElapsedTime(_ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        kern.append(ms.value)
+        _hip.hipEventDestroy(a)
+        _hip.hipEventDestroy(b)
+    kern_ms = np.array(kern)
     S = w.bytes_per_rank
     alg_bytes = w.algorithmic_bytes
     algbw = S / (ms_per_step / 1000.0) / 1e9
