@@ -171,3 +171,30 @@ def test_allreduce_tensors_wrapper():
     s.synchronize()
     for t in ins:
         assert np.array_equal(G.to_host_bits(t, "bf16"), want)
+
+
+def test_process_exits_cleanly_with_a_running_proxy():
+    """A process that used the port channel and exits without destroying its
+    channel set must still exit normally: the library stops every proxy
+    thread at exit, before the HIP runtime tears down."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import torch\n"
+        "from allreduce_emulated_peer_amd import mscl as M\n"
+        "M.channel_create(4, 0)\n"
+        "x = [torch.ones(1 << 16, device='cuda', dtype=torch.bfloat16) for _ in range(4)]\n"
+        "y = [torch.empty_like(t) for t in x]\n"
+        "M.allreduce_tensors(x, y, algo=M.ALGO_TWO_SHOT_PORT)\n"
+        "torch.cuda.synchronize()\n"
+        "assert bool((y[3] == 4).all())\n"
+        "print('done', flush=True)\n"
+    )
+    G.note("subprocess: port call, then exit with the proxy running")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "done" in r.stdout
+    assert "terminate" not in r.stderr and "Segmentation" not in r.stderr
