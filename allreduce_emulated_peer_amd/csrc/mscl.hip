@@ -72,7 +72,8 @@ const Config& config() {
     c.oneshot_max_bytes = env_size("MSCL_ONESHOT_MAX_BYTES", SIZE_MAX);  // SIZE_MAX: per-R table
     c.wg_target_total = env_size("MSCL_WG_TOTAL", 0);
     c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
-    c.wait_timeout_us = env_size("MSCL_WAIT_TIMEOUT_MS", 2000) * 1000;
+    // clamped to a day, so the microsecond count (and its tick count) cannot wrap
+    c.wait_timeout_us = std::min<size_t>(env_size("MSCL_WAIT_TIMEOUT_MS", 2000), size_t(86400000)) * 1000;
   });
   return c;
 }
@@ -777,7 +778,7 @@ mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t ch, uint64_t wait_t
   if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
   if (drop_signal_rank < -1 || drop_signal_rank >= ch->nranks)
     return fail(MSCL_ERR_INVALID_ARGUMENT, "drop_signal_rank must be -1 or a rank");
-  ch->wait_timeout_us = wait_timeout_us;
+  ch->wait_timeout_us = std::min<uint64_t>(wait_timeout_us, 86400000000ull);  // at most a day
   ch->drop_rank = drop_signal_rank;
   return MSCL_SUCCESS;
 }

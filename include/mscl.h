@@ -262,8 +262,8 @@ mscl_status_t mscl_channel_plan(mscl_channel_t channel, size_t count, mscl_dtype
 /*
  * Failure-handling controls for tests (never needed in normal use).
  *   wait_timeout_us : bound on every device-side wait() of later calls on
- *                     this set, in microseconds (0 restores the default of
- *                     MSCL_WAIT_TIMEOUT_MS or 2000 ms).
+ *                     this set, in microseconds, at most a day (0 restores
+ *                     the default of MSCL_WAIT_TIMEOUT_MS or 2000 ms).
  *   drop_signal_rank: -1 for normal operation; r in 0..R-1 makes rank r skip
  *                     its signal() in later calls, so its peers' wait()s run
  *                     into the bound and record TIMEOUT.  Every kernel still
