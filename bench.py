@@ -435,6 +435,25 @@ def main() -> int:
         del ri, ro
         torch.cuda.empty_cache()
 
+    size_curve = None
+    if not args.main_only:
+        # The metric's size range, R = 8 bf16 from 512 KiB to 128 MiB per rank,
+        # with AUTO's pick: device time per call from graph replay (hot buffers).
+        size_curve = {"note": "R=8 bf16, AUTO's pick, device time per call (graph replay, same buffers each call)"}
+        for k in range(19, 28):
+            cw = W.sweep_bf16(k)
+            ci_, co_ = device_inputs(cw), None
+            co_ = [torch.empty_like(t) for t in ci_]
+            t_c = graph_us(cw, ci_, co_, M.ALGO_AUTO, 50 if cw.bytes_per_rank <= (4 << 20) else 5)
+            pick = {1: "one_shot", 2: "two_shot", 3: "two_shot_fused"}[M.select_algo(cw.count, M.BFLOAT16, 8)]
+            size_curve[f"{cw.bytes_per_rank}B"] = {
+                "algo": pick, "us": round(t_c, 2), "algbw_GBps": round(cw.bytes_per_rank / t_c / 1e3, 1),
+                "pct_hbm_peak": round(100 * cw.algorithmic_bytes / t_c / 1e3 / HBM_PEAK_GBPS, 1)}
+            del ci_, co_
+            torch.cuda.empty_cache()
+        log(f"[bench] size curve: " + ", ".join(f"{k} {v['algbw_GBps']} GB/s" for k, v in size_curve.items()
+                                                 if k != "note"))
+
     port = None
     if not args.main_only:
         # The port channel (all-gather puts done by the host proxy on the SDMA
@@ -607,6 +626,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "latency": latency,
         "host_api": host,
+        "algbw_512KiB_to_128MiB": size_curve,
         "decode_512KiB": decode,
         "ragged_r16": ragged,
         "port_channel": port,
