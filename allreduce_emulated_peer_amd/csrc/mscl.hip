@@ -215,8 +215,13 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   }
   uint64_t want = std::max<uint64_t>(1, (vectors + tile - 1) / tile);
   // One workgroup per compute unit in total measured best for the streaming
-  // phases (fewer concurrent streams keep HBM pages open longer).
-  const uint64_t total = cfg.wg_target_total ? cfg.wg_target_total : static_cast<uint64_t>(ch->cus);
+  // phases (fewer concurrent streams keep HBM pages open longer).  The fused
+  // two-shot takes two in AUTO's middle band, up to kFusedMaxBytes per rank,
+  // where a rank's chunk is only a few tiles per workgroup (R = 8 bf16, 4 MiB:
+  // 12.2 -> 10.3 us); above it two are slower (128 MiB: 390 -> 401 us).
+  const bool fused_band = algo == MSCL_ALGO_TWO_SHOT_FUSED && count * elem_bytes(dtype) <= kFusedMaxBytes;
+  const uint64_t per_cu = fused_band ? 2 : 1;
+  const uint64_t total = cfg.wg_target_total ? cfg.wg_target_total : static_cast<uint64_t>(ch->cus) * per_cu;
   uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, total / R);
   cap = std::min<uint64_t>(cap, ch->slots);  // every workgroup of a barrier must be resident
   uint64_t b = std::min(want, cap);
