@@ -116,22 +116,22 @@ __device__ inline u32x4 reduce_partial(const KernelArgs& a, uint64_t vi, int nta
 // contiguous.  Full tiles (kFull) need no bounds checks, which keeps every
 // load of the tile issued back to back; the last, partial tile re-reads the
 // range's last vector in lanes past the end and skips their stores.
-template <int R, int U, bool kFull, bool kStream>
+template <int R, int U, bool kFull, bool kStream, int T = kThreads>
 __device__ inline void load_tile(u32x4 (&x)[U][R], const void* const* src, uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    uint64_t vi = base + static_cast<uint64_t>(u) * T;
     if (!kFull) vi = std::min<uint64_t>(vi, vend - 1);
 #pragma unroll
     for (int p = 0; p < R; ++p) x[u][p] = kStream ? load_vec_nt(src[p], vi) : load_vec(src[p], vi);
   }
 }
 
-template <int U, bool kFull, bool kStream>
+template <int U, bool kFull, bool kStream, int T = kThreads>
 __device__ inline void store_tile(void* dst, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t vi = base + static_cast<uint64_t>(u) * kThreads;
+    const uint64_t vi = base + static_cast<uint64_t>(u) * T;
     if (kFull || vi < vend) {
       if (kStream)
         store_vec_nt(dst, vi, y[u]);
@@ -435,17 +435,19 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_port(KernelArgs a) {
 // other rank reads or writes during the call, and in place the only reader
 // of in[p][chunk r] is rank r itself, each lane loading a vector from every
 // input before it stores that vector.
-template <class C, int R, int U, bool kFull>
+template <class C, int R, int U, bool kFull, int T>
 __device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
-  for (int p = 0; p < R; ++p) store_tile<U, kFull, true>(a.out[p], y, base, vend);
+  for (int p = 0; p < R; ++p) store_tile<U, kFull, true, T>(a.out[p], y, base, vend);
 }
 
-template <class C, int R>
-__global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
+// T threads per workgroup: 256, or 128 for messages too small to give every
+// CU two 256-lane tiles (more, smaller workgroups spread the loads).
+template <class C, int R, int T>
+__global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
   constexpr int V = C::V;
   constexpr int U = unroll_for<R>();
-  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  constexpr uint64_t kTile = static_cast<uint64_t>(T) * U;
   const int rank = blockIdx.x % R;
   const int slot = blockIdx.x / R;
   const uint64_t B = a.nblk;
@@ -463,15 +465,15 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
   if (static_cast<uint64_t>(slot) < nfull_tiles) {
     uint64_t t = slot;
     u32x4 cur[U][R];
-    load_tile<R, U, true, true>(cur, a.in, lane_base + t * kTile, v_full);
+    load_tile<R, U, true, true, T>(cur, a.in, lane_base + t * kTile, v_full);
     while (true) {
       const uint64_t tn = t + B;
       const bool more = tn < nfull_tiles;
       u32x4 nxt[U][R];
-      if (more) load_tile<R, U, true, true>(nxt, a.in, lane_base + tn * kTile, v_full);
+      if (more) load_tile<R, U, true, true, T>(nxt, a.in, lane_base + tn * kTile, v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
-      put_all_tile<C, R, U, true>(a, y, lane_base + t * kTile, v_full);
+      put_all_tile<C, R, U, true, T>(a, y, lane_base + t * kTile, v_full);
       if (!more) break;
       for (int u = 0; u < U; ++u)
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
@@ -482,9 +484,9 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_fused(KernelArgs a) {
     u32x4 x[U][R];
     u32x4 y[U];
     const uint64_t base = lane_base + nfull_tiles * kTile;
-    load_tile<R, U, false, true>(x, a.in, base, v_full);
+    load_tile<R, U, false, true, T>(x, a.in, base, v_full);
     reduce_tile<C, R, U>(y, x);
-    put_all_tile<C, R, U, false>(a, y, base, v_full);
+    put_all_tile<C, R, U, false, T>(a, y, base, v_full);
   }
   if (ntail != 0 && slot == 0 && threadIdx.x == 0) {
     const u32x4 y = reduce_partial<C, R>(a, v_full, ntail);
@@ -713,7 +715,8 @@ enum {
   kReduceScatterElem = 5,
   kAllGatherVec = 6,
   kAllGatherElem = 7,
-  kAlgoTwoShotPort = 8
+  kAlgoTwoShotPort = 8,
+  kAlgoTwoShotFusedHalf = 9  // the fused two-shot on kThreads / 2 threads per workgroup
 };
 
 template <class C, int R>
@@ -722,7 +725,8 @@ constexpr KernelFn kernel_for(int kind) {
     case kAlgoOneShot: return &mscl_oneshot<C, R, false>;
     case kAlgoOneShotInPlace: return &mscl_oneshot<C, R, true>;
     case kAlgoTwoShot: return &mscl_twoshot<C, R>;
-    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R>;
+    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R, kThreads>;
+    case kAlgoTwoShotFusedHalf: return &mscl_twoshot_fused<C, R, kThreads / 2>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
     case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;
@@ -750,5 +754,7 @@ inline KernelFn kernel_lookup(int kind, int dtype, int R) {
 }
 
 inline int unroll_for_runtime(int R) { return R <= 2 ? 4 : (R <= 4 ? 2 : 1); }
+
+inline int threads_for_kind(int kind) { return kind == kAlgoTwoShotFusedHalf ? kThreads / 2 : kThreads; }
 
 }  // namespace mscl

@@ -195,7 +195,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
                mscl_plan_t* plan) {
   const int R = ch->nranks;
   const uint64_t V = 16 / elem_bytes(dtype);
-  const uint64_t tile = static_cast<uint64_t>(kThreads) * unroll_for_runtime(R);
+  uint64_t tile = static_cast<uint64_t>(kThreads) * unroll_for_runtime(R);
   const Config& cfg = config();
   memset(plan, 0, sizeof(*plan));
   plan->algo = algo;
@@ -224,6 +224,17 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   const uint64_t total = cfg.wg_target_total ? cfg.wg_target_total : static_cast<uint64_t>(ch->cus) * per_cu;
   uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, total / R);
   cap = std::min<uint64_t>(cap, ch->slots);  // every workgroup of a barrier must be resident
+  if (fused_band && want < cap && want * R < static_cast<uint64_t>(ch->cus)) {
+    // Too few 256-lane tiles to give every compute unit one: halve the
+    // workgroup (and so the tile) to spread the loads over twice as many
+    // workgroups (R = 8 bf16, 512 KiB: 16 -> 32 per rank, 2.79 -> 2.72 us;
+    // R = 16 fp16, 256 KiB: 3.50 -> 3.13 us).  Where 256-lane tiles already
+    // reach every compute unit, halving measured slower (R = 4 fp32, 2 MiB:
+    // 3.19 -> 3.85 us).
+    plan->threads_per_workgroup = kThreads / 2;
+    tile /= 2;
+    want = std::max<uint64_t>(1, (vectors + tile - 1) / tile);
+  }
   uint64_t b = std::min(want, cap);
   if (algo == MSCL_ALGO_ONE_SHOT && cap >= kXcds)
     b = std::min((b + kXcds - 1) / kXcds * kXcds, cap / kXcds * kXcds);  // whole XCD groups
@@ -284,7 +295,7 @@ mscl_status_t launch(int kind, int dtype, int nranks, KernelArgs& a, void* strea
   if (!fn) return fail(MSCL_ERR_INVALID_ARGUMENT, "no kernel for this dtype and rank count");
   const dim3 grid(static_cast<unsigned>(nranks) * a.nblk);
   void* kargs[] = {&a};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(kThreads), kargs, 0,
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(threads_for_kind(kind)), kargs, 0,
                                  static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
@@ -567,7 +578,8 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
     a.port.fifo_mask = proxy::PortState::kEntries - 1;
   }
   const int kind = resolved == MSCL_ALGO_TWO_SHOT         ? kAlgoTwoShot
-                   : resolved == MSCL_ALGO_TWO_SHOT_FUSED ? kAlgoTwoShotFused
+                   : resolved == MSCL_ALGO_TWO_SHOT_FUSED
+                       ? (plan.threads_per_workgroup == kThreads ? kAlgoTwoShotFused : kAlgoTwoShotFusedHalf)
                    : resolved == MSCL_ALGO_TWO_SHOT_PORT  ? kAlgoTwoShotPort
                    : in_place                             ? kAlgoOneShotInPlace
                                                           : kAlgoOneShot;

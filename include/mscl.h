@@ -84,7 +84,7 @@ typedef struct {
   mscl_algo_t algo;          /* resolved algorithm (never AUTO) */
   int nranks;                /* R */
   int workgroups_per_rank;   /* B: workgroups (channel slots) per emulated rank */
-  int threads_per_workgroup; /* 256 */
+  int threads_per_workgroup; /* 256; 128 for a fused two-shot too small to give each workgroup a 256-lane tile */
   int vectors_per_thread;    /* 16-byte vectors each thread keeps in flight per rank buffer */
   int uses_barrier;          /* 1 when the kernel runs the signal/wait barrier */
   size_t chunk_elems;        /* two-shot: elements owned by each rank (a multiple of 16/elem_size) */

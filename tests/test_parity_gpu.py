@@ -369,6 +369,25 @@ def test_channel_registry():
         M.channel_destroy(a)
 
 
+@pytest.mark.parametrize("R,ns,dtype", [(8, (507_901, 520_193), "bf16"), (4, (516_093, 524_291), "fp32"),
+                                        (16, (491_517, 499_999), "fp16")])
+def test_fused_workgroup_sizes(R, ns, dtype):
+    """Both workgroup sizes of the fused two-shot at ragged counts on either
+    side of the switch from 128 to 256 threads, in place and out of place."""
+    h = G.channel(R)
+    seen = set()
+    for n in ns:
+        xs = P.rand_inputs(R, n, dtype, seed=n % 991)
+        want = O.allreduce(xs, dtype)
+        for in_place in (False, True):
+            plan = M.channel_plan(h, n, G.CODES[dtype], M.ALGO_TWO_SHOT_FUSED, in_place=in_place)
+            seen.add(plan.threads_per_workgroup)
+            G.note(f"fused R={R} n={n} {dtype} in_place={in_place} threads={plan.threads_per_workgroup}")
+            outs = G.run(xs, dtype, "two_shot_fused", in_place=in_place)
+            G.assert_matches_oracle(outs, want, dtype, f"fused R={R} n={n} in_place={in_place}")
+    assert seen == {128, 256}
+
+
 def test_plan_geometry():
     h = G.channel(8)
     p = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_AUTO)
@@ -385,6 +404,13 @@ def test_plan_geometry():
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 1
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
     assert q.uses_barrier == 0
+    # the fused two-shot halves its workgroups when 256-lane tiles cannot fill them
+    q = M.channel_plan(h, W.decode_bf16().count, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.threads_per_workgroup == 128 and q.workgroups_per_rank == 32
+    q = M.channel_plan(h, 2 << 20, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.threads_per_workgroup == 256
+    q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
+    assert q.threads_per_workgroup == 256
     q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_PORT)
     assert q.algo == M.ALGO_TWO_SHOT_PORT and q.uses_barrier == 0 and q.chunk_elems == p.chunk_elems
     r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
