@@ -31,7 +31,8 @@
 // the 8 XCDs, a rank's workgroups stay on a fixed XCD subset.  The one-shot
 // instead groups the R ranks of a slot on one XCD, because there every rank
 // re-reads the same input lines.  Each workgroup has 256 threads (4
-// wavefronts of 64); a tile is U 16-byte vectors per lane.
+// wavefronts of 64; the fused two-shot also comes in a 128-thread form for
+// small messages); a tile is U 16-byte vectors per lane.
 //
 // Two-shot chunks: rank r owns elements [r*c, min((r+1)*c, n)) with
 // c = roundup(ceil(n/R), V), V = 16 / element size.  Each lane handles the
@@ -442,7 +443,7 @@ __device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], ui
 }
 
 // T threads per workgroup: 256, or 128 for messages too small to give every
-// CU two 256-lane tiles (more, smaller workgroups spread the loads).
+// CU one 256-lane tile (more, smaller workgroups spread the loads).
 template <class C, int R, int T>
 __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
   constexpr int V = C::V;

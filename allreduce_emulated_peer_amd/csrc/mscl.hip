@@ -159,15 +159,17 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
   return MSCL_SUCCESS;
 }
 
-// AUTO's size bands, from device time per call (calls replayed from a graph)
-// on MI355X with bf16 buffers, for R = 2, 4, 8, 16:
-//   one-shot        up to oneshot_max_bytes(R): every size at R <= 2, 512 KiB
-//                   at R <= 4, 128 KiB at R <= 8, 64 KiB above (it reads R*S
-//                   per rank, from cache while the buffers fit);
-//   fused two-shot  up to 4 MiB: no barrier and no re-read, best in the middle
-//                   (R = 8, 1 MiB: 3.7 us against 5.2 two-shot, 6.4 one-shot);
+// AUTO's size bands, from device time per call on MI355X with bf16 buffers
+// (small sizes replayed from a graph, large ones timed over back-to-back calls):
+//   one-shot        up to oneshot_max_bytes(R): 64 MiB at R <= 2, 512 KiB at
+//                   R <= 4, 128 KiB at R <= 8, 64 KiB above (it reads R*S per
+//                   rank, from cache while the buffers fit: R = 2 out of place,
+//                   64 MiB 40.4 us against 44.9 fused, 80 MiB 75.1 against 56.1);
+//   fused two-shot  up to fused_max_bytes(R): no barrier and no re-read, best in
+//                   the middle (R = 8, 1 MiB: 3.7 us against 5.2 two-shot, 6.4
+//                   one-shot) and, with few ranks, at every size;
 //   two-shot        above: its separate read and write phases stream HBM best
-//                   (R = 8, 128 MiB: 376 us against 381 fused).
+//                   with many ranks (R = 8, 128 MiB: 376 us against 381 fused).
 // In place, the one-shot needs a barrier between each batch of tiles' loads
 // and stores (a rank overwrites an input its peers still read: R = 8,
 // 512 KiB, 7.3 us), while the fused two-shot needs none (2.9 us), so
@@ -175,20 +177,39 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
 size_t oneshot_max_bytes(int nranks) {
   const size_t env = config().oneshot_max_bytes;
   if (env != SIZE_MAX) return env;
-  if (nranks <= 2) return SIZE_MAX;
+  if (nranks <= 2) return size_t(64) << 20;
   if (nranks <= 4) return size_t(512) << 10;
   if (nranks <= 8) return size_t(128) << 10;
   return size_t(64) << 10;
 }
 
+// Up to this many bytes per rank buffer the fused two-shot also gets two
+// workgroups per compute unit (make_plan).
 constexpr size_t kFusedMaxBytes = size_t(4) << 20;
+
+// The fused two-shot's upper bound in AUTO.  With few ranks it beats the
+// two-shot at every size measured (128 MiB: R = 2 85.8 us against 96.7 in
+// place, 89.4 against 97.5 out of place; R = 5 in place 271 against 292); out
+// of place at R = 3, 4 and 6 the two-shot catches up at 128, 64 and 32 MiB
+// (R = 4, 128 MiB: 189.5 against 182.6); from R = 7 on it is ahead above
+// 4 MiB (R = 7 in place, 32 MiB: 105.0 against 113.2).
+size_t fused_max_bytes(int nranks, bool in_place) {
+  if (nranks <= 2 || (in_place && nranks <= 6)) return SIZE_MAX;
+  switch (nranks) {
+    case 3: return size_t(96) << 20;
+    case 4: return size_t(32) << 20;
+    case 5: return SIZE_MAX;
+    case 6: return size_t(8) << 20;
+  }
+  return kFusedMaxBytes;
+}
 
 mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo, bool in_place) {
   if (algo != MSCL_ALGO_AUTO) return static_cast<mscl_algo_t>(algo);
   const size_t bytes = count * elem_bytes(dtype);
   if (!in_place && bytes <= oneshot_max_bytes(nranks)) return MSCL_ALGO_ONE_SHOT;
   if (nranks == 1) return MSCL_ALGO_ONE_SHOT;  // a copy (or nothing, in place)
-  return bytes <= kFusedMaxBytes ? MSCL_ALGO_TWO_SHOT_FUSED : MSCL_ALGO_TWO_SHOT;
+  return bytes <= fused_max_bytes(nranks, in_place) ? MSCL_ALGO_TWO_SHOT_FUSED : MSCL_ALGO_TWO_SHOT;
 }
 
 void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t algo, bool in_place,

@@ -10,8 +10,9 @@
 // request is one put (`bytes` bytes from device address `src` to device
 // address `dst`) tagged with the rank whose completion counter the proxy
 // bumps once that copy has finished.  The proxy issues the copies on the
-// SDMA engines (hipMemcpyDeviceToDeviceNoCU) and checks each request's ranges
-// against the device allocations before it copies anything.
+// SDMA engines through HSA (a copy forced onto a given engine, completion
+// polled on an HSA signal) and checks each request's ranges against the
+// device allocations before it copies anything.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -238,15 +238,17 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
 /*
  * The algorithm MSCL_ALGO_AUTO resolves to for an out-of-place call of this
  * size (bytes = count * element size), from crossovers measured on MI355X:
- *   one-shot        bytes <= 512 KiB (R <= 4; every size at R <= 2),
+ *   one-shot        bytes <= 64 MiB (R <= 2), 512 KiB (R <= 4),
  *                   128 KiB (R <= 8), 64 KiB (R <= 16);
- *   fused two-shot  bytes <= 4 MiB;
+ *   fused two-shot  bytes <= 4 MiB (R >= 7), 8 MiB (R = 6), 32 MiB (R = 4),
+ *                   96 MiB (R = 3), every size (R = 2 and 5);
  *   two-shot        above.
  * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: in
  * place the one-shot needs a barrier between loads and stores, the fused
- * two-shot none.  Pure host
+ * two-shot none; in place the fused two-shot also takes every size at
+ * R <= 6 (mscl_channel_plan reports the in-place choice).  Pure host
  * computation.  MSCL_ONESHOT_MAX_BYTES (environment, read once) replaces the
- * one-shot limit for every R.  mscl_channel_plan reports the in-place choice.
+ * one-shot limit for every R.
  * Errors: INVALID_ARGUMENT.
  */
 mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, mscl_algo_t* out);

@@ -113,18 +113,28 @@ def test_size_overflow():
 
 
 def test_selector():
-    # one-shot up to a limit that falls with R, fused two-shot up to 4 MiB, two-shot above
+    # one-shot up to a limit that falls with R, fused two-shot up to a limit that falls with R, two-shot above
     KiB, MiB = 1024, 1024 * 1024
-    for R, limit in ((3, 512 * KiB), (4, 512 * KiB), (5, 128 * KiB), (8, 128 * KiB), (9, 64 * KiB), (16, 64 * KiB)):
+    fused_limit = {3: 96 * MiB, 4: 32 * MiB, 6: 8 * MiB, 7: 4 * MiB, 8: 4 * MiB, 9: 4 * MiB, 16: 4 * MiB}
+    for R, limit in ((3, 512 * KiB), (4, 512 * KiB), (5, 128 * KiB), (6, 128 * KiB), (7, 128 * KiB), (8, 128 * KiB),
+                     (9, 64 * KiB), (16, 64 * KiB)):
         assert M.select_algo(1, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
         assert M.select_algo(limit // 4, M.FLOAT32, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT_FUSED
-        assert M.select_algo(2 * MiB, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED  # 4 MiB per rank
-        assert M.select_algo(2 * MiB + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
-    for R in (1, 2):  # one-shot at every size
-        assert M.select_algo(2 ** 40, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
+        if R in fused_limit:
+            f = fused_limit[R]
+            assert M.select_algo(f // 2, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
+            assert M.select_algo(f // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
+            assert M.select_algo(f // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT
+        else:  # R = 5: fused at every size
+            assert M.select_algo(2 ** 40, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
+    assert M.select_algo(1, M.BFLOAT16, 1) == M.ALGO_ONE_SHOT
+    assert M.select_algo(2 ** 40, M.BFLOAT16, 1) == M.ALGO_ONE_SHOT  # one buffer: a copy at every size
+    assert M.select_algo(32 * MiB, M.BFLOAT16, 2) == M.ALGO_ONE_SHOT  # 64 MiB per rank
+    assert M.select_algo(32 * MiB + 1, M.BFLOAT16, 2) == M.ALGO_TWO_SHOT_FUSED
+    assert M.select_algo(2 ** 40, M.BFLOAT16, 2) == M.ALGO_TWO_SHOT_FUSED
     assert M.select_algo(4096, M.FLOAT32, 4) == M.ALGO_ONE_SHOT  # the 16 KiB integer workload
     assert M.select_algo(32 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT_FUSED  # 512 KiB decode shape
     assert M.select_algo(8192 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT  # 128 MiB prefill shape
