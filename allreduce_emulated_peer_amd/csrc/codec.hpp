@@ -122,6 +122,21 @@ __device__ inline void store_vec_nt(void* base, uint64_t vi, const u32x4& v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base) + vi);
 }
 
+// Device-scope temporal form, for puts whose destination is read soon by the
+// next kernel: the sc1 bit writes the line through this XCD's L2 to the
+// memory side at once (no dirty lines left for the end-of-kernel L2
+// write-back), and without the nt bit the Infinity Cache keeps it for the
+// reader.  Issued as a raw buffer store whose range is [base, base + nbytes):
+// the 32-bit byte offset limits it to buffers below 4 GiB, and a store past
+// nbytes is dropped by the hardware's range check instead of landing outside
+// the buffer.
+constexpr int kBufferSc1 = 1 << 4;                  // cache-policy operand: sc1
+constexpr int kRawBufferWord3 = 0x00020000;         // raw (untyped) buffer, 32-bit data format
+__device__ inline void store_vec_device(void* base, uint32_t nbytes, uint64_t vi, const u32x4& v) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, kRawBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, static_cast<uint32_t>(vi * 16), 0, kBufferSc1);
+}
+
 // First `nvalid` (< V) elements of vector `vi`; the rest read as zero bits.
 template <class C>
 __device__ inline u32x4 load_partial(const void* base, uint64_t vi, int nvalid) {

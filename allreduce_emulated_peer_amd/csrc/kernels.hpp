@@ -128,14 +128,23 @@ __device__ inline void load_tile(u32x4 (&x)[U][R], const void* const* src, uint6
   }
 }
 
-template <int U, bool kFull, bool kStream, int T = kThreads>
+// Store policy of a tile: cacheable (data re-read inside the call),
+// streaming (written once, not read soon), or device-scope temporal (a put
+// whose destination the next kernel reads while the call's buffers fit the
+// Infinity Cache; stores stay below vend, so vend * 16 bytes bound the range).
+enum class Put { kCached, kStream, kDevice };
+
+template <int U, bool kFull, Put kP, int T = kThreads>
 __device__ inline void store_tile(void* dst, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
+  const uint32_t range = static_cast<uint32_t>(std::min<uint64_t>(vend * 16, 0xFFFFFFFFull));
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint64_t vi = base + static_cast<uint64_t>(u) * T;
     if (kFull || vi < vend) {
-      if (kStream)
+      if constexpr (kP == Put::kStream)
         store_vec_nt(dst, vi, y[u]);
+      else if constexpr (kP == Put::kDevice)
+        store_vec_device(dst, range, vi, y[u]);
       else
         store_vec(dst, vi, y[u]);
     }
@@ -188,10 +197,10 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
       u32x4 y[U];
       if ((t + 1) * kTile <= nfull) {
         oneshot_reduce<C, R, U, true>(y, a, base, nfull);
-        store_tile<U, true, false>(dst, y, base, nfull);
+        store_tile<U, true, Put::kCached>(dst, y, base, nfull);
       } else {
         oneshot_reduce<C, R, U, false>(y, a, base, nfull);
-        store_tile<U, false, false>(dst, y, base, nfull);
+        store_tile<U, false, Put::kCached>(dst, y, base, nfull);
       }
     }
   } else {
@@ -218,9 +227,9 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
         const uint64_t t = t0 + h * B;
         const uint64_t base = t * kTile + threadIdx.x;
         if ((t + 1) * kTile <= nfull)
-          store_tile<U, true, false>(dst, y[h], base, nfull);
+          store_tile<U, true, Put::kCached>(dst, y[h], base, nfull);
         else if (t < ntiles)
-          store_tile<U, false, false>(dst, y[h], base, nfull);
+          store_tile<U, false, Put::kCached>(dst, y[h], base, nfull);
       }
     }
   }
@@ -233,17 +242,24 @@ __global__ __launch_bounds__(kThreads) void mscl_oneshot(KernelArgs a) {
   }
 }
 
-// Cache policy of the two-shot: inputs are read exactly once and the peers'
-// outputs written exactly once, so both stream past the caches; the rank's
-// own reduced chunk is written and read back, so it stays cacheable.
+// Cache policy of the two-shot: inputs are read exactly once, so they
+// stream past the caches; the rank's own reduced chunk is written and read
+// back, so it stays cacheable.  The peers' outputs are written once inside
+// the call; the put policy (streaming, or device-scope temporal when the
+// call's buffers fit the Infinity Cache and the next kernel will find the
+// outputs there) is a template parameter the host picks by size.
 constexpr bool kStreamRsLoads = true;
-constexpr bool kStreamAgStores = true;
 
-template <int R, int U, bool kFull>
+template <bool kCachedPuts>
+constexpr Put put_policy() {
+  return kCachedPuts ? Put::kDevice : Put::kStream;
+}
+
+template <int R, int U, bool kFull, Put kP>
 __device__ inline void ag_store(const KernelArgs& a, int rank, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int p = 0; p < R; ++p)  // put() to every peer, written once
-    if (p != rank) store_tile<U, kFull, kStreamAgStores>(a.out[p], y, base, vend);
+    if (p != rank) store_tile<U, kFull, kP>(a.out[p], y, base, vend);
 }
 
 template <int U, bool kFull>
@@ -304,7 +320,7 @@ __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& 
       if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, g.v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
-      store_tile<U, true, false>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather: cached
+      store_tile<U, true, Put::kCached>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather: cached
       if (!more) break;
       for (int u = 0; u < U; ++u)
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
@@ -317,15 +333,16 @@ __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& 
     const uint64_t base = lane_base + g.nfull_tiles * kTile;
     load_tile<R, U, false, kStreamRsLoads>(x, a.in, base, g.v_full);
     reduce_tile<C, R, U>(y, x);
-    store_tile<U, false, false>(mine, y, base, g.v_full);
+    store_tile<U, false, Put::kCached>(mine, y, base, g.v_full);
   }
   if (g.ntail != 0 && slot == 0 && threadIdx.x == 0)
     store_partial<C>(mine, g.v_full, reduce_partial<C, R>(a, g.v_full, g.ntail), g.ntail);
 }
 
-template <class C, int R>
+template <class C, int R, bool kCachedPuts>
 __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   constexpr int U = unroll_for<R>();
+  constexpr Put kP = put_policy<kCachedPuts>();
   constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
   const int rank = blockIdx.x % R;
   const int slot = blockIdx.x / R;
@@ -362,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
     u32x4 y[U];
     const uint64_t base = lane_base + nfull_tiles * kTile;
     ag_load<U, false>(y, mine, base, v_full);
-    ag_store<R, U, false>(a, rank, y, base, v_full);
+    ag_store<R, U, false, kP>(a, rank, y, base, v_full);
   }
   if (static_cast<uint64_t>(slot) < nfull_tiles) {
     uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
@@ -373,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
       const uint64_t tn = more ? t - B : t;
       u32x4 nxt[U];
       if (more) ag_load<U, true>(nxt, mine, lane_base + tn * kTile, v_full);
-      ag_store<R, U, true>(a, rank, cur, lane_base + t * kTile, v_full);
+      ag_store<R, U, true, kP>(a, rank, cur, lane_base + t * kTile, v_full);
       if (!more) break;
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
@@ -436,17 +453,18 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_port(KernelArgs a) {
 // other rank reads or writes during the call, and in place the only reader
 // of in[p][chunk r] is rank r itself, each lane loading a vector from every
 // input before it stores that vector.
-template <class C, int R, int U, bool kFull, int T>
+template <class C, int R, int U, bool kFull, int T, Put kP>
 __device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
-  for (int p = 0; p < R; ++p) store_tile<U, kFull, true, T>(a.out[p], y, base, vend);
+  for (int p = 0; p < R; ++p) store_tile<U, kFull, kP, T>(a.out[p], y, base, vend);
 }
 
 // T threads per workgroup: 256, or 128 for messages too small to give every
 // CU one 256-lane tile (more, smaller workgroups spread the loads).
-template <class C, int R, int T>
+template <class C, int R, int T, bool kCachedPuts>
 __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
   constexpr int V = C::V;
+  constexpr Put kP = put_policy<kCachedPuts>();
   constexpr int U = unroll_for<R>();
   constexpr uint64_t kTile = static_cast<uint64_t>(T) * U;
   const int rank = blockIdx.x % R;
@@ -474,7 +492,7 @@ __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
       if (more) load_tile<R, U, true, true, T>(nxt, a.in, lane_base + tn * kTile, v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
-      put_all_tile<C, R, U, true, T>(a, y, lane_base + t * kTile, v_full);
+      put_all_tile<C, R, U, true, T, kP>(a, y, lane_base + t * kTile, v_full);
       if (!more) break;
       for (int u = 0; u < U; ++u)
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
@@ -487,7 +505,7 @@ __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
     const uint64_t base = lane_base + nfull_tiles * kTile;
     load_tile<R, U, false, true, T>(x, a.in, base, v_full);
     reduce_tile<C, R, U>(y, x);
-    put_all_tile<C, R, U, false, T>(a, y, base, v_full);
+    put_all_tile<C, R, U, false, T, kP>(a, y, base, v_full);
   }
   if (ntail != 0 && slot == 0 && threadIdx.x == 0) {
     const u32x4 y = reduce_partial<C, R>(a, v_full, ntail);
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void mscl_reduce_scatter_kernel(KernelArg
         if (more) load_tile<R, U, true, true>(nxt, src, tn * kTile + lane, nv);
         u32x4 y[U];
         reduce_tile<C, R, U>(y, cur);
-        store_tile<U, true, false>(dst, y, t * kTile + lane, nv);
+        store_tile<U, true, Put::kCached>(dst, y, t * kTile + lane, nv);
         if (!more) break;
         for (int u = 0; u < U; ++u)
           for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
@@ -570,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void mscl_reduce_scatter_kernel(KernelArg
       const uint64_t base = nfull_tiles * kTile + lane;
       load_tile<R, U, false, true>(x, src, base, nv);
       reduce_tile<C, R, U>(y, x);
-      store_tile<U, false, false>(dst, y, base, nv);
+      store_tile<U, false, Put::kCached>(dst, y, base, nv);
     }
   } else {
     using Bits = typename C::Bits;
@@ -717,7 +735,11 @@ enum {
   kAllGatherVec = 6,
   kAllGatherElem = 7,
   kAlgoTwoShotPort = 8,
-  kAlgoTwoShotFusedHalf = 9  // the fused two-shot on kThreads / 2 threads per workgroup
+  kAlgoTwoShotFusedHalf = 9,  // the fused two-shot on kThreads / 2 threads per workgroup
+  // the same three with device-scope temporal puts (Put::kDevice)
+  kAlgoTwoShotCachedPuts = 10,
+  kAlgoTwoShotFusedCachedPuts = 11,
+  kAlgoTwoShotFusedHalfCachedPuts = 12
 };
 
 template <class C, int R>
@@ -725,9 +747,12 @@ constexpr KernelFn kernel_for(int kind) {
   switch (kind) {
     case kAlgoOneShot: return &mscl_oneshot<C, R, false>;
     case kAlgoOneShotInPlace: return &mscl_oneshot<C, R, true>;
-    case kAlgoTwoShot: return &mscl_twoshot<C, R>;
-    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R, kThreads>;
-    case kAlgoTwoShotFusedHalf: return &mscl_twoshot_fused<C, R, kThreads / 2>;
+    case kAlgoTwoShot: return &mscl_twoshot<C, R, false>;
+    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R, kThreads, false>;
+    case kAlgoTwoShotFusedHalf: return &mscl_twoshot_fused<C, R, kThreads / 2, false>;
+    case kAlgoTwoShotCachedPuts: return &mscl_twoshot<C, R, true>;
+    case kAlgoTwoShotFusedCachedPuts: return &mscl_twoshot_fused<C, R, kThreads, true>;
+    case kAlgoTwoShotFusedHalfCachedPuts: return &mscl_twoshot_fused<C, R, kThreads / 2, true>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
     case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;
@@ -756,6 +781,8 @@ inline KernelFn kernel_lookup(int kind, int dtype, int R) {
 
 inline int unroll_for_runtime(int R) { return R <= 2 ? 4 : (R <= 4 ? 2 : 1); }
 
-inline int threads_for_kind(int kind) { return kind == kAlgoTwoShotFusedHalf ? kThreads / 2 : kThreads; }
+inline int threads_for_kind(int kind) {
+  return (kind == kAlgoTwoShotFusedHalf || kind == kAlgoTwoShotFusedHalfCachedPuts) ? kThreads / 2 : kThreads;
+}
 
 }  // namespace mscl

@@ -58,6 +58,7 @@ struct Config {
   size_t wg_target_total;    // workgroups per launch, all ranks (0 = one per compute unit)
   size_t wg_per_rank;        // fixed workgroups per rank (0 = automatic)
   uint64_t wait_timeout_us;  // default bound of one device-side wait
+  size_t cached_puts_max_footprint;  // bound on 2*R*S for device-scope puts (SIZE_MAX = built-in)
 };
 
 const Config& config() {
@@ -67,6 +68,7 @@ const Config& config() {
     c.oneshot_max_bytes = env_size("MSCL_ONESHOT_MAX_BYTES", SIZE_MAX);  // SIZE_MAX: per-R table
     c.wg_target_total = env_size("MSCL_WG_TOTAL", 0);
     c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
+    c.cached_puts_max_footprint = env_size("MSCL_CACHED_PUTS_MAX_BYTES", SIZE_MAX);
     // clamped to a day, so the microsecond count (and its tick count) cannot wrap
     c.wait_timeout_us = std::min<size_t>(env_size("MSCL_WAIT_TIMEOUT_MS", 2000), size_t(86400000)) * 1000;
   });
@@ -192,7 +194,10 @@ constexpr size_t kFusedMaxBytes = size_t(4) << 20;
 // place, 89.4 against 97.5 out of place; R = 5 in place 271 against 292); out
 // of place at R = 3, 4 and 6 the two-shot catches up at 128, 64 and 32 MiB
 // (R = 4, 128 MiB: 189.5 against 182.6); from R = 7 on it is ahead above
-// 4 MiB (R = 7 in place, 32 MiB: 105.0 against 113.2).
+// 4 MiB (R = 7 in place, 32 MiB: 105.0 against 113.2), except at R = 8 up to
+// 8 MiB, where the fused kernel's device-scope puts (cached_puts) keep it in
+// front: 20.4 against 20.8 us with cached buffers, 24.9 against 26.4 with
+// uncached ones, 13.8 against 15.2 between a producer and a consumer kernel.
 size_t fused_max_bytes(int nranks, bool in_place) {
   if (nranks <= 2 || (in_place && nranks <= 6)) return SIZE_MAX;
   switch (nranks) {
@@ -200,6 +205,7 @@ size_t fused_max_bytes(int nranks, bool in_place) {
     case 4: return size_t(32) << 20;
     case 5: return SIZE_MAX;
     case 6: return size_t(8) << 20;
+    case 8: return size_t(8) << 20;
   }
   return kFusedMaxBytes;
 }
@@ -210,6 +216,27 @@ mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo, bool in_
   if (!in_place && bytes <= oneshot_max_bytes(nranks)) return MSCL_ALGO_ONE_SHOT;
   if (nranks == 1) return MSCL_ALGO_ONE_SHOT;  // a copy (or nothing, in place)
   return bytes <= fused_max_bytes(nranks, in_place) ? MSCL_ALGO_TWO_SHOT_FUSED : MSCL_ALGO_TWO_SHOT;
+}
+
+// Put policy of the two-shot kernels.  Their puts stream past the caches
+// unless the call's footprint (R inputs and R outputs, 2*R*S bytes) fits in
+// half of the 256 MiB Infinity Cache; then device-scope temporal stores
+// leave the outputs there for the kernel that reads them next.  Measured on
+// MI355X, bf16, with a producer kernel writing the inputs before each call
+// and a consumer kernel reading the outputs after it, replayed from a graph
+// (the call's share of the time, streaming -> device-scope puts): fused
+// two-shot R = 8 4 MiB 14.7 -> 11.1 us, 8 MiB 18.1 -> 13.8, R = 4 8 MiB
+// 15.2 -> 11.4, R = 16 2 MiB 13.3 -> 11.7; two-shot R = 8 8 MiB 20.2 -> 15.2.
+// With a 256 MiB footprint the gain is gone or reversed (fused R = 8 16 MiB
+// 39.1 -> 41.5, R = 16 8 MiB 34.6 -> 35.1) and calls whose buffers are not
+// cached pay 10-20% (two-shot R = 8 16 MiB 42.7 -> 51.1).
+constexpr size_t kCachedPutsMaxFootprint = size_t(128) << 20;
+bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
+  if (algo != MSCL_ALGO_TWO_SHOT && algo != MSCL_ALGO_TWO_SHOT_FUSED) return false;
+  if (bytes > (size_t(1) << 31)) return false;  // the buffer store's 32-bit byte range
+  const size_t env = config().cached_puts_max_footprint;
+  const size_t limit = env != SIZE_MAX ? env : kCachedPutsMaxFootprint;
+  return 2 * static_cast<size_t>(nranks) * bytes <= limit;
 }
 
 void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t algo, bool in_place,
@@ -223,6 +250,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   plan->nranks = R;
   plan->threads_per_workgroup = kThreads;
   plan->vectors_per_thread = unroll_for_runtime(R);
+  plan->cached_puts = cached_puts(algo, R, count * elem_bytes(dtype)) ? 1 : 0;
   uint64_t vectors;  // full vectors one rank covers
   if (algo == MSCL_ALGO_TWO_SHOT || algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_PORT) {
     const uint64_t per = (count + R - 1) / R;
@@ -460,7 +488,7 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
   // workgroup that has not been scheduled.
   int min_resident = 1 << 30;
   for (int dt = 0; dt < 3; ++dt) {
-    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot}) {
+    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot, kAlgoTwoShotCachedPuts}) {
       int per_cu = 0;
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)),
                                                        kThreads, 0);
@@ -598,9 +626,12 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
     a.port.arrived = ps->arrived;
     a.port.fifo_mask = proxy::PortState::kEntries - 1;
   }
-  const int kind = resolved == MSCL_ALGO_TWO_SHOT         ? kAlgoTwoShot
+  const bool cached = plan.cached_puts != 0;
+  const int kind = resolved == MSCL_ALGO_TWO_SHOT ? (cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot)
                    : resolved == MSCL_ALGO_TWO_SHOT_FUSED
-                       ? (plan.threads_per_workgroup == kThreads ? kAlgoTwoShotFused : kAlgoTwoShotFusedHalf)
+                       ? (plan.threads_per_workgroup == kThreads
+                              ? (cached ? kAlgoTwoShotFusedCachedPuts : kAlgoTwoShotFused)
+                              : (cached ? kAlgoTwoShotFusedHalfCachedPuts : kAlgoTwoShotFusedHalf))
                    : resolved == MSCL_ALGO_TWO_SHOT_PORT  ? kAlgoTwoShotPort
                    : in_place                             ? kAlgoOneShotInPlace
                                                           : kAlgoOneShot;

@@ -59,6 +59,7 @@ class Plan(ctypes.Structure):
         ("vectors_per_thread", ctypes.c_int),
         ("uses_barrier", ctypes.c_int),
         ("chunk_elems", ctypes.c_size_t),
+        ("cached_puts", ctypes.c_int),
     ]
 
 

@@ -454,6 +454,70 @@ def main() -> int:
         log(f"[bench] size curve: " + ", ".join(f"{k} {v['algbw_GBps']} GB/s" for k, v in size_curve.items()
                                                  if k != "note"))
 
+    pipeline = None
+    if not args.main_only:
+        # Tensor-parallel use: a producer kernel writes the inputs just before
+        # the call (the row-parallel GEMM's partial sums) and a consumer kernel
+        # reads the outputs just after it (the next layer).  Producer = copy from
+        # a source set into the inputs, consumer = copy from the outputs into a
+        # sink set, all replayed from one graph; the call's share of the time is
+        # (producer + call + consumer) - (producer + consumer), so it includes
+        # what the call's put policy saves or costs its neighbours.
+        pipeline = {"note": "R=8 bf16, AUTO's pick; us per iteration of producer (copy into the inputs), call, "
+                            "consumer (copy out of the outputs), replayed from one graph, 16 iterations, median of "
+                            "5 replays; allreduce_share_us = with_allreduce_us - producer_consumer_us"}
+        for k in (19, 22, 23, 24):  # 512 KiB, 4, 8 and 16 MiB per rank
+            pw = W.sweep_bf16(k)
+            src = device_inputs(pw)
+            pin = [torch.empty_like(t) for t in src]
+            pout = [torch.empty_like(t) for t in src]
+            sink = [torch.empty_like(t) for t in src]
+            reps = 16
+
+            def produce():
+                for a_, b_ in zip(pin, src):
+                    a_.copy_(b_)
+
+            def consume():
+                for a_, b_ in zip(sink, pout):
+                    a_.copy_(b_)
+
+            produce()
+            caller(pw, pin, pout)()
+            consume()
+            torch.cuda.synchronize()
+            res = {}
+            for with_call in (False, True):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    c = caller(pw, pin, pout, M.ALGO_AUTO, on_stream=torch.cuda.current_stream())
+                    for _ in range(reps):
+                        produce()
+                        if with_call:
+                            c()
+                        consume()
+                g.replay()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(5):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    g.replay()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b) * 1000.0 / reps)
+                res[with_call] = float(np.median(ts))
+                del g
+            pplan = M.channel_plan(M.channel_create(pw.nranks, dev), pw.count, M.BFLOAT16, M.ALGO_AUTO)
+            pipeline[f"{pw.bytes_per_rank}B"] = {
+                "algo": {1: "one_shot", 2: "two_shot", 3: "two_shot_fused"}[pplan.algo],
+                "cached_puts": pplan.cached_puts, "producer_consumer_us": round(res[False], 2),
+                "with_allreduce_us": round(res[True], 2), "allreduce_share_us": round(res[True] - res[False], 2)}
+            del src, pin, pout, sink
+            torch.cuda.empty_cache()
+        log(f"[bench] between producer and consumer: " + ", ".join(
+            f"{k} {v['allreduce_share_us']} us" for k, v in pipeline.items() if k != "note"))
+
     port = None
     if not args.main_only:
         # The port channel (all-gather puts done by the host proxy on the SDMA
@@ -628,6 +692,7 @@ def main() -> int:
         "host_api": host,
         "algbw_512KiB_to_128MiB": size_curve,
         "decode_512KiB": decode,
+        "between_producer_and_consumer": pipeline,
         "ragged_r16": ragged,
         "port_channel": port,
         "collectives": collectives,

@@ -88,6 +88,11 @@ typedef struct {
   int vectors_per_thread;    /* 16-byte vectors each thread keeps in flight per rank buffer */
   int uses_barrier;          /* 1 when the kernel runs the signal/wait barrier */
   size_t chunk_elems;        /* two-shot: elements owned by each rank (a multiple of 16/elem_size) */
+  int cached_puts;           /* two-shot kernels: 1 when the puts into the outputs are device-scope
+                                temporal stores (the call's 2*R*S bytes fit the Infinity Cache well,
+                                and the outputs stay there for their next reader), 0 when they
+                                stream past the caches.  MSCL_CACHED_PUTS_MAX_BYTES (environment,
+                                read once) replaces the built-in bound on 2*R*S */
 } mscl_plan_t;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -173,6 +178,12 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * pointer tables travel in the kernel arguments.
  * A failure recorded by an earlier call (see mscl_channel_check) makes this
  * call return that code without launching, until mscl_channel_reset().
+ * Cache policy of the two-shot kernels' puts: when the call's footprint
+ * (R inputs + R outputs, 2*R*count*element size) is at most 128 MiB they
+ * are device-scope temporal stores, which leave the outputs in the
+ * Infinity Cache for the kernel that reads them next; above that they
+ * stream past the caches (mscl_channel_plan reports the choice).  It
+ * changes time only, never results.
  * MSCL_ALGO_TWO_SHOT_PORT follows the pages' PortChannel (MSCCL++ README, Key
  * Concepts, "PortChannel and MemoryChannel", "Host-Side Communication
  * Proxy"): GPU threads only post requests, and a CPU proxy moves the data
@@ -240,8 +251,8 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
  * size (bytes = count * element size), from crossovers measured on MI355X:
  *   one-shot        bytes <= 64 MiB (R <= 2), 512 KiB (R <= 4),
  *                   128 KiB (R <= 8), 64 KiB (R <= 16);
- *   fused two-shot  bytes <= 4 MiB (R >= 7), 8 MiB (R = 6), 32 MiB (R = 4),
- *                   96 MiB (R = 3), every size (R = 2 and 5);
+ *   fused two-shot  bytes <= 4 MiB (R = 7 and R >= 9), 8 MiB (R = 6 and 8),
+ *                   32 MiB (R = 4), 96 MiB (R = 3), every size (R = 2 and 5);
  *   two-shot        above.
  * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: in
  * place the one-shot needs a barrier between loads and stores, the fused

@@ -388,6 +388,24 @@ def test_fused_workgroup_sizes(R, ns, dtype):
     assert seen == {128, 256}
 
 
+@pytest.mark.parametrize("algo", ["two_shot", "two_shot_fused"])
+def test_put_policies_at_the_cache_bound(algo):
+    """The two-shot kernels in both put policies: R = 8 bf16 at 8 MiB per rank
+    (2*R*S = 128 MiB: device-scope puts) and one vector more (streaming puts),
+    out of place and in place, against the oracle."""
+    R, dtype = 8, "bf16"
+    h = G.channel(R)
+    for n, cached in (((8 << 20) // 2, 1), ((8 << 20) // 2 + 8, 0)):
+        xs = P.rand_inputs(R, n, dtype, seed=n % 997)
+        want = O.allreduce(xs, dtype)
+        for in_place in (False, True):
+            plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_CODES[algo], in_place=in_place)
+            assert plan.cached_puts == cached
+            G.note(f"{algo} R={R} n={n} in_place={in_place} cached_puts={cached}")
+            outs = G.run(xs, dtype, algo, in_place=in_place)
+            G.assert_matches_oracle(outs, want, dtype, f"{algo} n={n} in_place={in_place}")
+
+
 def test_plan_geometry():
     h = G.channel(8)
     p = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_AUTO)
@@ -413,5 +431,16 @@ def test_plan_geometry():
     assert q.threads_per_workgroup == 256
     q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_PORT)
     assert q.algo == M.ALGO_TWO_SHOT_PORT and q.uses_barrier == 0 and q.chunk_elems == p.chunk_elems
+    # device-scope puts while the call's 2*R*S bytes fit in 128 MiB, streaming puts above
+    assert p.cached_puts == 0
+    mib8 = (8 << 20) // 2
+    q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_AUTO)
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.cached_puts == 1
+    q = M.channel_plan(h, mib8 + 8, M.BFLOAT16, M.ALGO_AUTO)
+    assert q.algo == M.ALGO_TWO_SHOT and q.cached_puts == 0
+    q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.cached_puts == 1
+    for algo in (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_PORT):  # not a put policy of theirs
+        assert M.channel_plan(h, mib8, M.BFLOAT16, algo).cached_puts == 0
     r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
     assert r16.chunk_elems % 8 == 0 and r16.chunk_elems * 16 >= W.ragged_outliers_bf16().count
