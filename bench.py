@@ -297,7 +297,7 @@ def main() -> int:
     log(f"[bench] {ms_per_step:.4f} ms/step wall, kernel mean {kern_ms.mean():.4f} ms (p50 {np.median(kern_ms):.4f}),"
         f" algbw {algbw:.1f} GB/s, {hbm_gbps:.1f} GB/s algorithmic HBM ({100 * hbm_gbps / HBM_PEAK_GBPS:.1f}% of peak)")
     traffic = committed_traffic()
-    roofline = {"bound": "hbm", "kernel": "mscl_twoshot<BF16, 8>", "achieved": round(achieved, 1),
+    roofline = {"bound": "hbm", "kernel": "mscl_twoshot<BF16, 8, false>", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if traffic is None else int(traffic), "traffic_unit": "bytes per launch",
                 "traffic_gbps": None if traffic is None else round(traffic / (kern_ms.mean() / 1000.0) / 1e9, 1),
