@@ -194,17 +194,21 @@ constexpr size_t kFusedMaxBytes = size_t(4) << 20;
 // place, 89.4 against 97.5 out of place; R = 5 in place 271 against 292); out
 // of place at R = 3, 4 and 6 the two-shot catches up at 128, 64 and 32 MiB
 // (R = 4, 128 MiB: 189.5 against 182.6); from R = 7 on it is ahead above
-// 4 MiB (R = 7 in place, 32 MiB: 105.0 against 113.2), except at R = 8 up to
-// 8 MiB, where the fused kernel's device-scope puts (cached_puts) keep it in
-// front: 20.4 against 20.8 us with cached buffers, 24.9 against 26.4 with
-// uncached ones, 13.8 against 15.2 between a producer and a consumer kernel.
+// 4 MiB (R = 7 in place, 32 MiB: 105.0 against 113.2).  Up to 8 MiB at R = 7
+// and 8, and 16 MiB at R = 6, the fused kernel stays in front, with its
+// device-scope puts (cached_puts) below 128 MiB of footprint: R = 8, 8 MiB,
+// 20.4 against 20.8 us with cached buffers, 24.9 against 26.4 with uncached
+// ones, 13.8 against 15.2 between a producer and a consumer kernel; R = 7,
+// 8 MiB, 23.4 / 31.3 / 19.9 against 23.4 / 38.9 / 21.1; R = 6, 16 MiB,
+// 44.6 / 42.7 / 43.3 against 44.2 / 43.4 / 48.0.
 size_t fused_max_bytes(int nranks, bool in_place) {
   if (nranks <= 2 || (in_place && nranks <= 6)) return SIZE_MAX;
   switch (nranks) {
     case 3: return size_t(96) << 20;
     case 4: return size_t(32) << 20;
     case 5: return SIZE_MAX;
-    case 6: return size_t(8) << 20;
+    case 6: return size_t(16) << 20;
+    case 7:
     case 8: return size_t(8) << 20;
   }
   return kFusedMaxBytes;

@@ -251,8 +251,9 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
  * size (bytes = count * element size), from crossovers measured on MI355X:
  *   one-shot        bytes <= 64 MiB (R <= 2), 512 KiB (R <= 4),
  *                   128 KiB (R <= 8), 64 KiB (R <= 16);
- *   fused two-shot  bytes <= 4 MiB (R = 7 and R >= 9), 8 MiB (R = 6 and 8),
- *                   32 MiB (R = 4), 96 MiB (R = 3), every size (R = 2 and 5);
+ *   fused two-shot  bytes <= 4 MiB (R >= 9), 8 MiB (R = 7 and 8),
+ *                   16 MiB (R = 6), 32 MiB (R = 4), 96 MiB (R = 3), every
+ *                   size (R = 2 and 5);
  *   two-shot        above.
  * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: in
  * place the one-shot needs a barrier between loads and stores, the fused

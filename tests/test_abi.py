@@ -115,7 +115,7 @@ def test_size_overflow():
 def test_selector():
     # one-shot up to a limit that falls with R, fused two-shot up to a limit that falls with R, two-shot above
     KiB, MiB = 1024, 1024 * 1024
-    fused_limit = {3: 96 * MiB, 4: 32 * MiB, 6: 8 * MiB, 7: 4 * MiB, 8: 8 * MiB, 9: 4 * MiB, 16: 4 * MiB}
+    fused_limit = {3: 96 * MiB, 4: 32 * MiB, 6: 16 * MiB, 7: 8 * MiB, 8: 8 * MiB, 9: 4 * MiB, 16: 4 * MiB}
     for R, limit in ((3, 512 * KiB), (4, 512 * KiB), (5, 128 * KiB), (6, 128 * KiB), (7, 128 * KiB), (8, 128 * KiB),
                      (9, 64 * KiB), (16, 64 * KiB)):
         assert M.select_algo(1, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
