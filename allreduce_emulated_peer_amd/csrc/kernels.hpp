@@ -132,11 +132,14 @@ __device__ inline void load_tile(u32x4 (&x)[U][R], const void* const* src, uint6
 // streaming (written once, not read soon), or device-scope temporal (a put
 // whose destination the next kernel reads while the call's buffers fit the
 // Infinity Cache; stores stay below vend, so vend * 16 bytes bound the range).
+// The host uses the device-scope form only for buffers below 2 GiB; should a
+// larger range ever reach it, the range is zero and its stores are dropped
+// rather than written at a wrapped 32-bit offset.
 enum class Put { kCached, kStream, kDevice };
 
 template <int U, bool kFull, Put kP, int T = kThreads>
 __device__ inline void store_tile(void* dst, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
-  const uint32_t range = static_cast<uint32_t>(std::min<uint64_t>(vend * 16, 0xFFFFFFFFull));
+  const uint32_t range = vend * 16 <= 0xFFFFFFFFull ? static_cast<uint32_t>(vend * 16) : 0u;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint64_t vi = base + static_cast<uint64_t>(u) * T;
