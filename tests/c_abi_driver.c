@@ -71,6 +71,8 @@ static int run(int R, int dtype, size_t count, int algo, const char* in_path, co
 
   mscl_channel_t ch;
   MSCL_OK(mscl_channel_create(R, 0, &ch));
+  mscl_plan_t plan;
+  MSCL_OK(mscl_channel_plan(ch, count, (mscl_dtype_t)dtype, (mscl_algo_t)algo, in_place, &plan));
   const int reps = in_place ? 1 : 3;
   for (int i = 0; i < reps; ++i)
     MSCL_OK(mscl_allreduce((const void* const*)in, (void* const*)out, count, (mscl_dtype_t)dtype, R,
@@ -95,7 +97,8 @@ static int run(int R, int dtype, size_t count, int algo, const char* in_path, co
   }
   HIP_OK(hipStreamDestroy(stream));
   free(host);
-  printf("ok R=%d dtype=%d count=%zu algo=%d%s\n", R, dtype, count, algo, in_place ? " in place" : "");
+  printf("ok R=%d dtype=%d count=%zu algo=%d%s plan_algo=%d cached_puts=%d\n", R, dtype, count, algo,
+         in_place ? " in place" : "", (int)plan.algo, plan.cached_puts);
   return 0;
 }
 

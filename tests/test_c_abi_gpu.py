@@ -29,10 +29,34 @@ CASES = [
     (5, "bf16", 300_001, "normal", "two_shot_port", False),
 ]
 
+# The put policy forced by MSCL_CACHED_PUTS_MAX_BYTES (read once per process,
+# so these run the driver with it set): streaming puts at sizes whose default
+# is device-scope puts, and device-scope puts at a size whose default is
+# streaming; (case, environment value, expected cached_puts of the plan).
+ENV_CASES = [
+    ((8, "bf16", 1_000_003, "normal", "two_shot_fused", False), "0", 0),
+    ((8, "bf16", 1_000_003, "normal", "two_shot", True), "0", 0),
+    ((4, "fp16", 9_000_001, "uniform", "two_shot", False), "1000000000", 1),
+]
 
-@pytest.mark.parametrize("R,dtype,n,dist,algo,in_place", CASES,
-                         ids=[f"r{c[0]}_{c[1]}_{c[2]}_{c[4]}{'_inplace' if c[5] else ''}" for c in CASES])
+
+def _case_id(c):
+    return f"r{c[0]}_{c[1]}_{c[2]}_{c[4]}{'_inplace' if c[5] else ''}"
+
+
+@pytest.mark.parametrize("R,dtype,n,dist,algo,in_place", CASES, ids=[_case_id(c) for c in CASES])
 def test_c_driver_matches_oracle(tmp_path, R, dtype, n, dist, algo, in_place):
+    _run_driver(tmp_path, R, dtype, n, dist, algo, in_place)
+
+
+@pytest.mark.parametrize("case,limit,cached", ENV_CASES,
+                         ids=[f"{_case_id(c)}_cached_puts_max_{v}" for c, v, _ in ENV_CASES])
+def test_c_driver_put_policy_override(tmp_path, case, limit, cached):
+    out = _run_driver(tmp_path, *case, env={"MSCL_CACHED_PUTS_MAX_BYTES": limit})
+    assert f"cached_puts={cached}" in out, out
+
+
+def _run_driver(tmp_path, R, dtype, n, dist, algo, in_place, env=None):
     assert os.path.exists(DRIVER), "tests/c_abi_driver is not built: run __graft_entry__.build()"
     w = W.custom(R, dtype, n, dist, seed_index=11)
     xs = W.generate_all(w)
@@ -44,7 +68,8 @@ def test_c_driver_matches_oracle(tmp_path, R, dtype, n, dist, algo, in_place):
     if in_place:
         args.append("inplace")
     print(f"[gpu-case] c driver {' '.join(args[1:5])} {'in place' if in_place else ''}", flush=True)
-    r = subprocess.run(args, capture_output=True, text=True, timeout=120)
+    r = subprocess.run(args, capture_output=True, text=True, timeout=120,
+                       env=None if env is None else {**os.environ, **env})
     assert r.returncode == 0, f"driver failed ({r.returncode}): {r.stderr}"
     got = np.fromfile(dst, dtype=STORAGE[dtype]).reshape(R, n)
     want = O.bits_of(O.allreduce(xs, dtype), dtype)
@@ -52,3 +77,4 @@ def test_c_driver_matches_oracle(tmp_path, R, dtype, n, dist, algo, in_place):
         if not np.array_equal(got[rank], want):
             bad = np.nonzero(O.ulp_distance(got[rank], want, dtype))[0]
             raise AssertionError(f"rank {rank}: {bad.size} elements differ, first at {bad[:8].tolist()}")
+    return r.stdout
