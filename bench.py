@@ -221,6 +221,21 @@ def main() -> int:
     def p50_us_timing_events(call, iters):
         return bracket_us(call, iters)
 
+    def batch_us(call, iters):
+        """Mean time per call of `iters` back-to-back eager calls between two
+        events (the way collective benchmarks usually report latency: launch
+        throughput and device time overlap, the events are paid once)."""
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1000.0 / iters
+
     def graph_us(w, ins, outs, algo=M.ALGO_AUTO, reps=100):
         """Device time per call: `reps` calls captured in one HIP graph and
         replayed, so the host launch cost is amortised (median of 5 replays)."""
@@ -313,11 +328,13 @@ def main() -> int:
         p50, mean = p50_us(caller(lw, li, lo), args.latency_iters)
         p50_te = p50_us_timing_events(caller(lw, li, lo), args.latency_iters)
         dev_us = graph_us(lw, li, lo)
+        b_us = batch_us(caller(lw, li, lo), args.latency_iters)
         latency[f"p50_us_16KiB_{lw.name}"] = round(p50, 2)
         latency[f"p50_us_timing_events_16KiB_{lw.name}"] = round(p50_te, 2)
         latency[f"graph_us_per_call_16KiB_{lw.name}"] = round(dev_us, 2)
+        latency[f"batch_us_per_call_16KiB_{lw.name}"] = round(b_us, 2)
         log(f"[bench] {lw.name}: p50 {p50:.2f} us per call (torch events), {p50_te:.2f} us (timing-only events), "
-            f"{dev_us:.2f} us per call replayed from a graph")
+            f"{dev_us:.2f} us per call replayed from a graph, {b_us:.2f} us per call over back-to-back eager calls")
     if latency:
         # latency floor: the smallest event p50 over the R = 8 bf16 sizes up to 64 KiB
         floor = {}
@@ -332,7 +349,8 @@ def main() -> int:
         latency["floor_at_bytes"] = best
         latency["note"] = ("p50_us: torch (HIP) events around each call; p50_us_timing_events: HIP events created "
                            "with hipEventDisableSystemFence around each call; graph_us_per_call: 100 calls "
-                           "replayed from one graph (device time per call); floor: smallest torch-event p50 over "
+                           "replayed from one graph (device time per call); batch_us_per_call: torch events around "
+                           "back-to-back eager calls, divided by their number; floor: smallest torch-event p50 over "
                            "1, 4, 16 and 64 KiB per rank")
     host = None
     if not args.main_only:
