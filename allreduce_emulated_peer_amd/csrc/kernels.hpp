@@ -302,18 +302,38 @@ __device__ inline Chunk chunk_of(const KernelArgs& a, int rank, int slot) {
   return g;
 }
 
-// Reduce-scatter: chunk `rank` of every input -> own output `mine`.
+// Reduced tiles one workgroup of the held two-shot keeps in LDS: 40 tiles of
+// 256 lanes x 16 bytes = 160 KiB, all of a gfx950 compute unit's LDS.
+constexpr int kHeldTiles = 40;
+
+// A slot's full tiles t = slot, slot + B, ... (all below nfull_tiles), of
+// which the newest `held` ones (j >= first_held, j counting the slot's tiles
+// from 0) stay in LDS instead of going to the rank's own output.
+struct Held {
+  u32x4 (*lds)[kThreads];  // [kHeldTiles][kThreads], or null: nothing held
+  uint64_t first_held;
+};
+
+__device__ inline Held held_range(u32x4 (*lds)[kThreads], uint64_t nfull_tiles, int slot, uint64_t B) {
+  if (!lds || static_cast<uint64_t>(slot) >= nfull_tiles) return Held{lds, ~0ull};
+  const uint64_t nts = (nfull_tiles - 1 - slot) / B + 1;
+  return Held{lds, nts > kHeldTiles ? nts - kHeldTiles : 0};
+}
+
+// Reduce-scatter: chunk `rank` of every input -> own output `mine` (or, for
+// the tiles `h` names, this lane's LDS slots).
 // Software pipelined: the loads of the slot's next tile are issued before
 // the current tile is reduced and stored, so each wave keeps R*U 16-byte
 // loads in flight while it computes.
-template <class C, int R>
+template <class C, int R, bool kHold = false>
 __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& g, int slot, void* mine,
-                                              uint64_t lane_base) {
+                                              uint64_t lane_base, const Held h = Held{nullptr, ~0ull}) {
   constexpr int U = unroll_for<R>();
   constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
   const uint64_t B = a.nblk;
   if (static_cast<uint64_t>(slot) < g.nfull_tiles) {
     uint64_t t = slot;
+    uint64_t j = 0;  // index of t among this slot's tiles
     u32x4 cur[U][R];
     load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * kTile, g.v_full);
     while (true) {
@@ -323,7 +343,16 @@ __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& 
       if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, g.v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
-      store_tile<U, true, Put::kCached>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather: cached
+      if constexpr (kHold && U == 1) {
+        if (j >= h.first_held) {
+          h.lds[j - h.first_held][threadIdx.x] = y[0];  // kept for the all-gather, read back by this lane only
+        } else {
+          store_tile<U, true, Put::kCached>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather
+        }
+      } else {
+        store_tile<U, true, Put::kCached>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather
+      }
+      ++j;
       if (!more) break;
       for (int u = 0; u < U; ++u)
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
@@ -342,8 +371,8 @@ __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& 
     store_partial<C>(mine, g.v_full, reduce_partial<C, R>(a, g.v_full, g.ntail), g.ntail);
 }
 
-template <class C, int R, bool kCachedPuts>
-__global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
+template <class C, int R, bool kCachedPuts, bool kHold>
+__device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads]) {
   constexpr int U = unroll_for<R>();
   constexpr Put kP = put_policy<kCachedPuts>();
   constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
@@ -358,7 +387,8 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   void* const mine = a.out[rank];
   const uint64_t lane_base = g.v_lo + threadIdx.x;
 
-  twoshot_reduce_scatter<C, R>(a, g, slot, mine, lane_base);
+  const Held h = held_range(lds, nfull_tiles, slot, B);
+  twoshot_reduce_scatter<C, R, kHold>(a, g, slot, mine, lane_base, h);
   const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
 
   // signal / wait with the same slot of every peer rank.  Arrival only: no
@@ -386,6 +416,22 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
   }
   if (static_cast<uint64_t>(slot) < nfull_tiles) {
     uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
+    if constexpr (kHold && U == 1) {
+      if (h.lds) {
+        // The held tiles (the newest) come from LDS and go to the rank's own
+        // output as well as to every peer's.
+        const uint64_t nts = (nfull_tiles - 1 - slot) / B + 1;
+        for (uint64_t j = nts; j-- > h.first_held;) {
+          u32x4 y[U];
+          y[0] = h.lds[j - h.first_held][threadIdx.x];
+          const uint64_t base = lane_base + (slot + j * B) * kTile;
+          store_tile<U, true, kP>(mine, y, base, v_full);
+          ag_store<R, U, true, kP>(a, rank, y, base, v_full);
+        }
+        if (h.first_held == 0) return;
+        t = slot + (h.first_held - 1) * B;  // the newest tile not held
+      }
+    }
     u32x4 cur[U];
     ag_load<U, true>(cur, mine, lane_base + t * kTile, v_full);
     while (true) {
@@ -399,6 +445,33 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       t = tn;
     }
+  }
+}
+
+template <class C, int R, bool kCachedPuts>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
+  twoshot_body<C, R, kCachedPuts, false>(a, nullptr);
+}
+
+// The two-shot with each workgroup's newest reduced tiles (up to kHeldTiles
+// per lane, 160 KiB) kept in LDS across the barrier: those tiles skip the
+// store to the rank's own output during the reduce-scatter and its re-read
+// during the all-gather, which writes them to every output, the rank's own
+// included, so the call moves 2*R*S bytes when a workgroup's whole share is
+// held.  Its LDS leaves room for one workgroup per compute unit.  Measured on
+// MI355X, R = 8 bf16, where the host uses it (16 to 40 tiles per workgroup):
+// 16 MiB 44.3 -> 43.3 us, 32 MiB 92.0 -> 87.2 us; R = 16: 16 MiB 93.1 -> 89.2
+// us, 32 MiB 191.2 -> 178.1 us.  Holding part of a larger share gains
+// nothing (R = 8, 128 MiB, 40 of 128 tiles: 375 -> 377 us), and with fewer
+// tiles the all-gather's extra own-output store costs more than it saves
+// (R = 16, 8 MiB, 8 tiles: 47.7 -> 49.0 us).
+template <class C, int R>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot_held(KernelArgs a) {
+  if constexpr (unroll_for<R>() == 1) {
+    __shared__ u32x4 held[kHeldTiles][kThreads];
+    twoshot_body<C, R, false, true>(a, held);
+  } else {
+    twoshot_body<C, R, false, false>(a, nullptr);  // several vectors per lane: the host never picks this
   }
 }
 
@@ -742,7 +815,8 @@ enum {
   // the same three with device-scope temporal puts (Put::kDevice)
   kAlgoTwoShotCachedPuts = 10,
   kAlgoTwoShotFusedCachedPuts = 11,
-  kAlgoTwoShotFusedHalfCachedPuts = 12
+  kAlgoTwoShotFusedHalfCachedPuts = 12,
+  kAlgoTwoShotHeld = 13  // the two-shot keeping reduced tiles in LDS (mscl_twoshot_held)
 };
 
 template <class C, int R>
@@ -756,6 +830,7 @@ constexpr KernelFn kernel_for(int kind) {
     case kAlgoTwoShotCachedPuts: return &mscl_twoshot<C, R, true>;
     case kAlgoTwoShotFusedCachedPuts: return &mscl_twoshot_fused<C, R, kThreads, true>;
     case kAlgoTwoShotFusedHalfCachedPuts: return &mscl_twoshot_fused<C, R, kThreads / 2, true>;
+    case kAlgoTwoShotHeld: return &mscl_twoshot_held<C, R>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
     case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;

@@ -59,6 +59,7 @@ struct Config {
   size_t wg_per_rank;        // fixed workgroups per rank (0 = automatic)
   uint64_t wait_timeout_us;  // default bound of one device-side wait
   size_t cached_puts_max_footprint;  // bound on 2*R*S for device-scope puts (SIZE_MAX = built-in)
+  bool two_shot_hold;                // the two-shot may keep reduced tiles in LDS (mscl_twoshot_held)
 };
 
 const Config& config() {
@@ -69,6 +70,7 @@ const Config& config() {
     c.wg_target_total = env_size("MSCL_WG_TOTAL", 0);
     c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
     c.cached_puts_max_footprint = env_size("MSCL_CACHED_PUTS_MAX_BYTES", SIZE_MAX);
+    c.two_shot_hold = env_size("MSCL_TWO_SHOT_HOLD", 1) != 0;
     // clamped to a day, so the microsecond count (and its tick count) cannot wrap
     c.wait_timeout_us = std::min<size_t>(env_size("MSCL_WAIT_TIMEOUT_MS", 2000), size_t(86400000)) * 1000;
   });
@@ -83,6 +85,7 @@ struct mscl_channel_s {
   int refcount = 0;
   int cus = 0;
   uint32_t slots = 0;            // barrier slots allocated per rank (= max co-resident workgroups per rank)
+  uint32_t held_slots = 0;       // the same bound for the two-shot that keeps tiles in LDS (one per CU)
   uint64_t wall_clock_khz = 100000;
   uint32_t* inbound = nullptr;   // device [R][R][slots]
   uint32_t* consumed = nullptr;  // device [R][slots]
@@ -235,6 +238,12 @@ mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo, bool in_
 // 39.1 -> 41.5, R = 16 8 MiB 34.6 -> 35.1) and calls whose buffers are not
 // cached pay 10-20% (two-shot R = 8 16 MiB 42.7 -> 51.1).
 constexpr size_t kCachedPutsMaxFootprint = size_t(128) << 20;
+
+// Fewest full tiles per workgroup for which the held two-shot pays (below, its
+// all-gather's store of the held tiles to the rank's own output costs more
+// than the skipped store and re-read save: R = 16, 8 MiB, 8 tiles, 47.7 ->
+// 49.0 us; R = 8, 16 MiB, 16 tiles, 44.3 -> 43.3 us).
+constexpr uint64_t kHeldMinTiles = 16;
 bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
   if (algo != MSCL_ALGO_TWO_SHOT && algo != MSCL_ALGO_TWO_SHOT_FUSED) return false;
   if (bytes > (size_t(1) << 31)) return false;  // the buffer store's 32-bit byte range
@@ -292,6 +301,16 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   if (algo == MSCL_ALGO_ONE_SHOT && cap >= kXcds)
     b = std::min((b + kXcds - 1) / kXcds * kXcds, cap / kXcds * kXcds);  // whole XCD groups
   plan->workgroups_per_rank = static_cast<int>(b);
+  // The two-shot keeps every workgroup's reduced tiles in LDS across the
+  // barrier (mscl_twoshot_held) when its whole share fits there and is large
+  // enough to pay for the all-gather's extra store: 16 to kHeldTiles full
+  // tiles per workgroup, one vector per lane, one workgroup per compute unit.
+  if (algo == MSCL_ALGO_TWO_SHOT && !plan->cached_puts && cfg.two_shot_hold && plan->vectors_per_thread == 1 &&
+      b <= ch->held_slots) {
+    const uint64_t per_slot = (vectors / tile + b - 1) / b;  // full tiles of the busiest workgroup
+    if (per_slot >= kHeldMinTiles && per_slot <= static_cast<uint64_t>(kHeldTiles))
+      plan->held_tiles = static_cast<int>(per_slot);
+  }
 }
 
 // The channel set for (current device, R) and its per-call controls.
@@ -505,6 +524,21 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
     }
   }
   ch->slots = static_cast<uint32_t>(std::max(1, std::min(min_resident / nranks, 4096)));
+  // The held two-shot's 160 KiB of LDS leaves room for one workgroup per
+  // compute unit; it gets its own bound so that the other kernels keep theirs.
+  int held_resident = 1 << 30;
+  for (int dt = 0; dt < 3; ++dt) {
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(kernel_lookup(kAlgoTwoShotHeld, dt, nranks)), kThreads, 0);
+    if (e != hipSuccess) {
+      delete ch;
+      (void)hipSetDevice(prev);
+      return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    }
+    held_resident = std::min(held_resident, per_cu * ch->cus);
+  }
+  ch->held_slots = static_cast<uint32_t>(std::min<int>(held_resident / nranks, static_cast<int>(ch->slots)));
   const size_t inbound_bytes = sizeof(uint32_t) * nranks * nranks * ch->slots;
   const size_t consumed_bytes = sizeof(uint32_t) * nranks * ch->slots;
   mscl_status_t st = MSCL_SUCCESS;
@@ -631,7 +665,8 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
     a.port.fifo_mask = proxy::PortState::kEntries - 1;
   }
   const bool cached = plan.cached_puts != 0;
-  const int kind = resolved == MSCL_ALGO_TWO_SHOT ? (cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot)
+  const int kind = resolved == MSCL_ALGO_TWO_SHOT
+                       ? (plan.held_tiles ? kAlgoTwoShotHeld : cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot)
                    : resolved == MSCL_ALGO_TWO_SHOT_FUSED
                        ? (plan.threads_per_workgroup == kThreads
                               ? (cached ? kAlgoTwoShotFusedCachedPuts : kAlgoTwoShotFused)

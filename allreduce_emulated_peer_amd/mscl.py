@@ -60,6 +60,7 @@ class Plan(ctypes.Structure):
         ("uses_barrier", ctypes.c_int),
         ("chunk_elems", ctypes.c_size_t),
         ("cached_puts", ctypes.c_int),
+        ("held_tiles", ctypes.c_int),
     ]
 
 

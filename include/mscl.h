@@ -93,6 +93,10 @@ typedef struct {
                                 and the outputs stay there for their next reader), 0 when they
                                 stream past the caches.  MSCL_CACHED_PUTS_MAX_BYTES (environment,
                                 read once) replaces the built-in bound on 2*R*S */
+  int held_tiles;            /* two-shot: reduced tiles per lane each workgroup keeps in LDS across the
+                                barrier instead of storing and re-reading them (its whole share, 16 to
+                                40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
+                                turns it off */
 } mscl_plan_t;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */

@@ -29,14 +29,19 @@ CASES = [
     (5, "bf16", 300_001, "normal", "two_shot_port", False),
 ]
 
-# The put policy forced by MSCL_CACHED_PUTS_MAX_BYTES (read once per process,
-# so these run the driver with it set): streaming puts at sizes whose default
-# is device-scope puts, and device-scope puts at a size whose default is
-# streaming; (case, environment value, expected cached_puts of the plan).
+# Plan controls read from the environment once per process, so these run the
+# driver with them set: the put policy forced by MSCL_CACHED_PUTS_MAX_BYTES
+# (streaming puts at sizes whose default is device-scope puts, device-scope
+# puts at a size whose default is streaming), and the two-shot's LDS hold
+# with its default and turned off by MSCL_TWO_SHOT_HOLD=0; (case, environment,
+# what the driver must report about the plan).
 ENV_CASES = [
-    ((8, "bf16", 1_000_003, "normal", "two_shot_fused", False), "0", 0),
-    ((8, "bf16", 1_000_003, "normal", "two_shot", True), "0", 0),
-    ((4, "fp16", 9_000_001, "uniform", "two_shot", False), "1000000000", 1),
+    ((8, "bf16", 1_000_003, "normal", "two_shot_fused", False), {"MSCL_CACHED_PUTS_MAX_BYTES": "0"}, "cached_puts=0"),
+    ((8, "bf16", 1_000_003, "normal", "two_shot", True), {"MSCL_CACHED_PUTS_MAX_BYTES": "0"}, "cached_puts=0"),
+    ((4, "fp16", 9_000_001, "uniform", "two_shot", False), {"MSCL_CACHED_PUTS_MAX_BYTES": "1000000000"},
+     "cached_puts=1"),
+    ((8, "bf16", 12_000_007, "normal", "auto", False), {}, "held_tiles=23"),
+    ((8, "bf16", 12_000_007, "normal", "two_shot", True), {"MSCL_TWO_SHOT_HOLD": "0"}, "held_tiles=0"),
 ]
 
 
@@ -49,11 +54,12 @@ def test_c_driver_matches_oracle(tmp_path, R, dtype, n, dist, algo, in_place):
     _run_driver(tmp_path, R, dtype, n, dist, algo, in_place)
 
 
-@pytest.mark.parametrize("case,limit,cached", ENV_CASES,
-                         ids=[f"{_case_id(c)}_cached_puts_max_{v}" for c, v, _ in ENV_CASES])
-def test_c_driver_put_policy_override(tmp_path, case, limit, cached):
-    out = _run_driver(tmp_path, *case, env={"MSCL_CACHED_PUTS_MAX_BYTES": limit})
-    assert f"cached_puts={cached}" in out, out
+@pytest.mark.parametrize("case,env,expect", ENV_CASES,
+                         ids=[f"{_case_id(c)}_{'_'.join(f'{k}={v}' for k, v in e.items()) or 'default'}"
+                              for c, e, _ in ENV_CASES])
+def test_c_driver_plan_controls(tmp_path, case, env, expect):
+    out = _run_driver(tmp_path, *case, env=env)
+    assert expect in out, out
 
 
 def _run_driver(tmp_path, R, dtype, n, dist, algo, in_place, env=None):

@@ -406,6 +406,25 @@ def test_put_policies_at_the_cache_bound(algo):
             G.assert_matches_oracle(outs, want, dtype, f"{algo} n={n} in_place={in_place}")
 
 
+@pytest.mark.parametrize("R,n", [(8, 8 << 20), (8, 12_000_007), (16, 8 << 20)],
+                         ids=["r8_16MiB", "r8_ragged_24MB", "r16_16MiB"])
+def test_two_shot_held_in_lds(R, n):
+    """The two-shot that keeps each workgroup's reduced tiles in LDS across
+    the barrier (16 to 40 full tiles per workgroup), bf16, out of place and in
+    place, against the oracle; the ragged size adds a partial tile and a
+    partial vector to the held ones."""
+    dtype = "bf16"
+    h = G.channel(R)
+    xs = P.rand_inputs(R, n, dtype, seed=n % 983)
+    want = O.allreduce(xs, dtype)
+    for in_place in (False, True):
+        plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_TWO_SHOT, in_place=in_place)
+        assert 16 <= plan.held_tiles <= 40 and plan.cached_puts == 0
+        G.note(f"two_shot held R={R} n={n} in_place={in_place} held_tiles={plan.held_tiles}")
+        outs = G.run(xs, dtype, "two_shot", in_place=in_place)
+        G.assert_matches_oracle(outs, want, dtype, f"two_shot held R={R} n={n} in_place={in_place}")
+
+
 def test_plan_geometry():
     h = G.channel(8)
     p = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_AUTO)
@@ -432,15 +451,18 @@ def test_plan_geometry():
     q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_PORT)
     assert q.algo == M.ALGO_TWO_SHOT_PORT and q.uses_barrier == 0 and q.chunk_elems == p.chunk_elems
     # device-scope puts while the call's 2*R*S bytes fit in 128 MiB, streaming puts above
-    assert p.cached_puts == 0
+    assert p.cached_puts == 0 and p.held_tiles == 0  # 128 tiles per workgroup: more than LDS holds
+    q = M.channel_plan(h, (32 << 20) // 2, M.BFLOAT16, M.ALGO_AUTO)
+    assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 32
     mib8 = (8 << 20) // 2
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.cached_puts == 1
     q = M.channel_plan(h, mib8 + 8, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_TWO_SHOT and q.cached_puts == 0
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_TWO_SHOT)
-    assert q.cached_puts == 1
+    assert q.cached_puts == 1 and q.held_tiles == 0  # 8 tiles per workgroup: too few to hold
     for algo in (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_PORT):  # not a put policy of theirs
         assert M.channel_plan(h, mib8, M.BFLOAT16, algo).cached_puts == 0
     r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert r16.held_tiles == 32
     assert r16.chunk_elems % 8 == 0 and r16.chunk_elems * 16 >= W.ragged_outliers_bf16().count
