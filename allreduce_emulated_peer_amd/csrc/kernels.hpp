@@ -305,6 +305,7 @@ __device__ inline Chunk chunk_of(const KernelArgs& a, int rank, int slot) {
 // Reduced tiles one workgroup of the held two-shot keeps in LDS: 40 tiles of
 // 256 lanes x 16 bytes = 160 KiB, all of a gfx950 compute unit's LDS.
 constexpr int kHeldTiles = 40;
+constexpr int kStatusInvalid = 1;  // MSCL_ERR_INVALID_ARGUMENT in the channel's status word
 
 // A slot's full tiles t = slot, slot + B, ... (all below nfull_tiles), of
 // which the newest `held` ones (j >= first_held, j counting the slot's tiles
@@ -415,23 +416,29 @@ __device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads])
     ag_store<R, U, false, kP>(a, rank, y, base, v_full);
   }
   if (static_cast<uint64_t>(slot) < nfull_tiles) {
-    uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
-    if constexpr (kHold && U == 1) {
-      if (h.lds) {
-        // The held tiles (the newest) come from LDS and go to the rank's own
-        // output as well as to every peer's.
-        const uint64_t nts = (nfull_tiles - 1 - slot) / B + 1;
-        for (uint64_t j = nts; j-- > h.first_held;) {
-          u32x4 y[U];
-          y[0] = h.lds[j - h.first_held][threadIdx.x];
-          const uint64_t base = lane_base + (slot + j * B) * kTile;
-          store_tile<U, true, kP>(mine, y, base, v_full);
-          ag_store<R, U, true, kP>(a, rank, y, base, v_full);
-        }
-        if (h.first_held == 0) return;
-        t = slot + (h.first_held - 1) * B;  // the newest tile not held
-      }
+  if constexpr (kHold && U == 1) {
+    // Every full tile of this slot is in LDS: the all-gather writes each to
+    // the rank's own output and to every peer's.  The host launches this
+    // kernel only when a workgroup's whole share fits (at most kHeldTiles
+    // tiles); a share that does not is recorded as a failed call, not served
+    // in part.  (The partial form, with the remaining tiles re-read and put
+    // by the pipelined loop below, gained nothing where measured, and the
+    // ROCm 7.2 compiler built that loop wrongly in this kernel: its select
+    // of the next tile read a carry flag left by an unrelated add.)
+    if (h.first_held != 0) {
+      if (threadIdx.x == 0) __hip_atomic_store(a.ch.status, kStatusInvalid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      return;
     }
+    const uint64_t nts = (nfull_tiles - 1 - slot) / B + 1;
+    for (uint64_t j = nts; j-- > 0;) {
+      u32x4 y[U];
+      y[0] = h.lds[j][threadIdx.x];
+      const uint64_t base = lane_base + (slot + j * B) * kTile;
+      store_tile<U, true, kP>(mine, y, base, v_full);
+      ag_store<R, U, true, kP>(a, rank, y, base, v_full);
+    }
+  } else {
+    uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
     u32x4 cur[U];
     ag_load<U, true>(cur, mine, lane_base + t * kTile, v_full);
     while (true) {
@@ -445,6 +452,7 @@ __device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads])
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       t = tn;
     }
+  }
   }
 }
 
