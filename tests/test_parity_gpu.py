@@ -406,8 +406,9 @@ def test_put_policies_at_the_cache_bound(algo):
             G.assert_matches_oracle(outs, want, dtype, f"{algo} n={n} in_place={in_place}")
 
 
-@pytest.mark.parametrize("R,n", [(8, 8 << 20), (8, 12_000_007), (16, 8 << 20)],
-                         ids=["r8_16MiB", "r8_ragged_24MB", "r16_16MiB"])
+@pytest.mark.parametrize("R,n", [(8, 8 << 20), (8, 12_000_007), (16, 8 << 20), (5, 9_000_001), (7, 10_000_003),
+                                 (12, 8_000_009)],
+                         ids=["r8_16MiB", "r8_ragged_24MB", "r16_16MiB", "r5_ragged", "r7_ragged", "r12_ragged"])
 def test_two_shot_held_in_lds(R, n):
     """The two-shot that keeps each workgroup's reduced tiles in LDS across
     the barrier (16 to 40 full tiles per workgroup), bf16, out of place and in
