@@ -253,7 +253,7 @@ bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
 }
 
 void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t algo, bool in_place,
-               mscl_plan_t* plan) {
+               mscl_plan_t* plan, bool allow_slices = true) {
   const int R = ch->nranks;
   const uint64_t V = 16 / elem_bytes(dtype);
   uint64_t tile = static_cast<uint64_t>(kThreads) * unroll_for_runtime(R);
@@ -305,11 +305,40 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   // barrier (mscl_twoshot_held) when its whole share fits there and is large
   // enough to pay for the all-gather's extra store: 16 to kHeldTiles full
   // tiles per workgroup, one vector per lane, one workgroup per compute unit.
+  plan->slices = 1;
+  plan->slice_elems = count;
   if (algo == MSCL_ALGO_TWO_SHOT && !plan->cached_puts && cfg.two_shot_hold && plan->vectors_per_thread == 1 &&
       b <= ch->held_slots) {
     const uint64_t per_slot = (vectors / tile + b - 1) / b;  // full tiles of the busiest workgroup
-    if (per_slot >= kHeldMinTiles && per_slot <= static_cast<uint64_t>(kHeldTiles))
+    if (per_slot >= kHeldMinTiles && per_slot <= static_cast<uint64_t>(kHeldTiles)) {
       plan->held_tiles = static_cast<int>(per_slot);
+    } else if (per_slot > static_cast<uint64_t>(kHeldTiles) && allow_slices) {
+      // Too large to hold: run the call as consecutive slices, each a
+      // complete two-shot whose shares fit in LDS.  Slice boundaries keep
+      // every rank's chunk a whole number of tiles (chunks that start off a
+      // 4 KiB tile boundary measured far slower: R = 8, 128 MiB in 25.6 MiB
+      // slices 417 us against 364 in 32 MiB ones).  Shares of 16 tiles
+      // measured best with up to 8 ranks (R = 8, 128 MiB: 8 slices 352 us,
+      // 4 slices 360-364, one call 378), the fewest slices that fit with
+      // more (R = 16, 128 MiB: 4 slices 712-725 us, 8 slices 729-748, one
+      // call 770-815).
+      const uint64_t tile_elems = tile * V;
+      const uint64_t unit = static_cast<uint64_t>(R) * tile_elems;
+      uint64_t k = R <= 8 ? per_slot / kHeldMinTiles : (per_slot + kHeldTiles - 1) / kHeldTiles;
+      for (; k >= 2 && k <= 1024; ++k) {
+        const uint64_t m = ((count + k - 1) / k + unit - 1) / unit * unit;
+        mscl_plan_t first;
+        make_plan(ch, m, dtype, algo, in_place, &first, /*allow_slices=*/false);
+        if (first.held_tiles == 0) {
+          if ((m / unit + first.workgroups_per_rank - 1) / first.workgroups_per_rank < kHeldMinTiles) break;
+          continue;  // a share still too large: one slice more
+        }
+        *plan = first;
+        plan->slice_elems = m;
+        plan->slices = static_cast<int>((count + m - 1) / m);
+        break;
+      }
+    }
   }
 }
 
@@ -663,6 +692,30 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
     a.port.issued = ps->issued;
     a.port.arrived = ps->arrived;
     a.port.fifo_mask = proxy::PortState::kEntries - 1;
+  }
+  if (plan.slices > 1) {
+    // Consecutive slices, each a complete two-shot on its own element range
+    // (an AllReduce is elementwise, so the result is the same), planned and
+    // launched in stream order on the same channel set.
+    const size_t e = elem_bytes(dtype);
+    for (size_t lo = 0; lo < count; lo += plan.slice_elems) {
+      const size_t c = std::min(plan.slice_elems, count - lo);
+      const void* sin[kMaxRanks];
+      void* sout[kMaxRanks];
+      for (int r = 0; r < nranks; ++r) {
+        sin[r] = static_cast<const char*>(inputs[r]) + lo * e;
+        sout[r] = static_cast<char*>(outputs[r]) + lo * e;
+      }
+      mscl_plan_t sp;
+      make_plan(b.ch, c, dtype, resolved, in_place, &sp, /*allow_slices=*/false);
+      KernelArgs sa;
+      fill_args(&sa, b, sin, sout, nranks, c);
+      sa.chunk = sp.chunk_elems;
+      sa.nblk = static_cast<uint32_t>(sp.workgroups_per_rank);
+      const int kind = sp.held_tiles ? kAlgoTwoShotHeld : sp.cached_puts ? kAlgoTwoShotCachedPuts : kAlgoTwoShot;
+      if ((st = launch(kind, dtype, nranks, sa, stream)) != MSCL_SUCCESS) return st;
+    }
+    return MSCL_SUCCESS;
   }
   const bool cached = plan.cached_puts != 0;
   const int kind = resolved == MSCL_ALGO_TWO_SHOT

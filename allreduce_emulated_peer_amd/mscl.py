@@ -61,6 +61,8 @@ class Plan(ctypes.Structure):
         ("chunk_elems", ctypes.c_size_t),
         ("cached_puts", ctypes.c_int),
         ("held_tiles", ctypes.c_int),
+        ("slices", ctypes.c_int),
+        ("slice_elems", ctypes.c_size_t),
     ]
 
 

@@ -96,7 +96,12 @@ typedef struct {
   int held_tiles;            /* two-shot: reduced tiles per lane each workgroup keeps in LDS across the
                                 barrier instead of storing and re-reading them (its whole share, 16 to
                                 40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
-                                turns it off */
+                                turns it off, and the slicing below with it */
+  int slices;                /* kernel launches the call runs as: 1, or, for a two-shot too large for its
+                                shares to fit in LDS, consecutive slices of slice_elems elements (the
+                                last one shorter), each a complete two-shot; the fields above then
+                                describe the first slice */
+  size_t slice_elems;        /* elements per slice (count when slices == 1) */
 } mscl_plan_t;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -176,12 +181,16 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  *             _TWO_SHOT_PORT.  All give bit-identical results.
  *   stream  : hipStream_t on the current device (NULL = default stream).
  * Every pointer must be 16-byte aligned and on the current device.  The call
- * is asynchronous: it validates, launches one kernel on `stream` and
- * returns.  The caller owns all buffers and keeps them alive until the stream
+ * is asynchronous: it validates, launches one kernel on `stream` (one per
+ * slice for a large two-shot, below) and returns.  The caller owns all buffers and keeps them alive until the stream
  * has finished.  Nothing is allocated or copied to the device per call: the
  * pointer tables travel in the kernel arguments.
  * A failure recorded by an earlier call (see mscl_channel_check) makes this
  * call return that code without launching, until mscl_channel_reset().
+ * A two-shot whose per-workgroup shares are too large to keep in LDS runs
+ * as consecutive slices of every buffer, each a complete two-shot on its own
+ * element range, launched back to back on `stream` (mscl_channel_plan
+ * reports the slices); the result is the same, as the sum is elementwise.
  * Cache policy of the two-shot kernels' puts: when the call's footprint
  * (R inputs + R outputs, 2*R*count*element size) is at most 128 MiB they
  * are device-scope temporal stores, which leave the outputs in the

@@ -426,11 +426,30 @@ def test_two_shot_held_in_lds(R, n):
         G.assert_matches_oracle(outs, want, dtype, f"two_shot held R={R} n={n} in_place={in_place}")
 
 
+@pytest.mark.parametrize("R,n", [(8, 24_000_017), (16, 22_000_001), (5, 30_000_007)],
+                         ids=["r8_ragged_48MB", "r16_ragged_44MB", "r5_ragged_60MB"])
+def test_two_shot_in_held_slices(R, n):
+    """A two-shot too large for its shares to fit in LDS runs as consecutive
+    tile-aligned slices, each a complete held two-shot; the last slice is
+    ragged.  bf16, out of place and in place, against the oracle."""
+    dtype = "bf16"
+    h = G.channel(R)
+    xs = P.rand_inputs(R, n, dtype, seed=n % 977)
+    want = O.allreduce(xs, dtype)
+    for in_place in (False, True):
+        plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_TWO_SHOT, in_place=in_place)
+        assert plan.slices >= 2 and 16 <= plan.held_tiles <= 40
+        assert plan.slice_elems % (R * 2048) == 0 and (plan.slices - 1) * plan.slice_elems < n <= plan.slices * plan.slice_elems
+        G.note(f"two_shot sliced R={R} n={n} in_place={in_place} slices={plan.slices} held_tiles={plan.held_tiles}")
+        outs = G.run(xs, dtype, "two_shot", in_place=in_place)
+        G.assert_matches_oracle(outs, want, dtype, f"two_shot sliced R={R} n={n} in_place={in_place}")
+
+
 def test_plan_geometry():
     h = G.channel(8)
     p = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_AUTO)
     assert p.algo == M.ALGO_TWO_SHOT and p.uses_barrier == 1 and p.threads_per_workgroup == 256
-    assert p.chunk_elems == W.prefill_bf16().count // 8
+    assert p.chunk_elems == p.slice_elems // 8
     assert 1 <= p.workgroups_per_rank
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 0
@@ -450,9 +469,11 @@ def test_plan_geometry():
     q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
     assert q.threads_per_workgroup == 256
     q = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT_PORT)
-    assert q.algo == M.ALGO_TWO_SHOT_PORT and q.uses_barrier == 0 and q.chunk_elems == p.chunk_elems
+    assert q.algo == M.ALGO_TWO_SHOT_PORT and q.uses_barrier == 0 and q.slices == 1
+    assert q.chunk_elems == W.prefill_bf16().count // 8
     # device-scope puts while the call's 2*R*S bytes fit in 128 MiB, streaming puts above
-    assert p.cached_puts == 0 and p.held_tiles == 0  # 128 tiles per workgroup: more than LDS holds
+    # 128 tiles per workgroup, more than LDS holds: 8 slices of 16 MiB, 16 tiles each
+    assert p.cached_puts == 0 and p.slices == 8 and p.slice_elems == (16 << 20) // 2 and p.held_tiles == 16
     q = M.channel_plan(h, (32 << 20) // 2, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 32
     mib8 = (8 << 20) // 2
