@@ -303,6 +303,46 @@ def test_graph_capture_and_replay():
         del g
 
 
+def test_graph_capture_of_held_and_sliced_two_shots():
+    """A held two-shot (one launch) and a sliced one (several launches, each
+    with its own barrier) captured in HIP graphs and replayed with eager work
+    between replays; then an eager call on the same channel set."""
+    R = 8
+    h = G.channel(R)
+    for n in (8 << 20, 24_000_017):  # 16 MiB: held; ~48 MB ragged: 2 held slices
+        plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_TWO_SHOT)
+        assert plan.held_tiles >= 16 and plan.slices == (1 if n == 8 << 20 else 2)
+        xs = P.rand_inputs(R, n, "bf16", seed=n % 971)
+        want = O.allreduce(xs, "bf16")
+        ins = [G.to_device(x, "bf16") for x in xs]
+        outs = [G.poison_like(t) for t in ins]
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R,
+                        M.ALGO_TWO_SHOT, s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R,
+                        M.ALGO_TWO_SHOT, torch.cuda.current_stream().cuda_stream)
+        for rep in range(5):
+            for o in outs:
+                o.zero_()
+            G.note(f"graph replay {rep} n={n} slices={plan.slices}")
+            g.replay()
+            torch.cuda.synchronize()
+            G.assert_matches_oracle(outs, want, "bf16", f"graph replay {rep} n={n}")
+        for _ in range(20):
+            g.replay()
+        torch.cuda.synchronize()
+        G.assert_matches_oracle(outs, want, "bf16", f"after 25 replays n={n}")
+        outs2 = G.run(xs, "bf16", "two_shot", dev_inputs=ins)
+        G.assert_matches_oracle(outs2, want, "bf16", f"eager after replays n={n}")
+        del g, ins, outs, outs2
+
+
 @pytest.mark.parametrize("algo,in_place", [(M.ALGO_TWO_SHOT, False), (M.ALGO_ONE_SHOT, True),
                                            (M.ALGO_TWO_SHOT_PORT, False)])
 def test_timeout_is_reported_not_hung(algo, in_place):
