@@ -304,11 +304,14 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   // The two-shot keeps every workgroup's reduced tiles in LDS across the
   // barrier (mscl_twoshot_held) when its whole share fits there and is large
   // enough to pay for the all-gather's extra store: 16 to kHeldTiles full
-  // tiles per workgroup, one vector per lane, one workgroup per compute unit.
+  // tiles per workgroup, one vector per lane, one workgroup per compute unit,
+  // from R = 6 up (R = 5, where AUTO never takes the two-shot, measured
+  // 3-4% slower held at 24-40 MiB and 2% faster sliced at 64-128 MiB; R = 6
+  // and 7 gain 8-13% sliced at 64-128 MiB: R = 7, 128 MiB, 404 -> 350 us).
   plan->slices = 1;
   plan->slice_elems = count;
   if (algo == MSCL_ALGO_TWO_SHOT && !plan->cached_puts && cfg.two_shot_hold && plan->vectors_per_thread == 1 &&
-      b <= ch->held_slots) {
+      R >= 6 && b <= ch->held_slots) {
     const uint64_t per_slot = (vectors / tile + b - 1) / b;  // full tiles of the busiest workgroup
     if (per_slot >= kHeldMinTiles && per_slot <= static_cast<uint64_t>(kHeldTiles)) {
       plan->held_tiles = static_cast<int>(per_slot);

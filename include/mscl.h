@@ -93,9 +93,9 @@ typedef struct {
                                 and the outputs stay there for their next reader), 0 when they
                                 stream past the caches.  MSCL_CACHED_PUTS_MAX_BYTES (environment,
                                 read once) replaces the built-in bound on 2*R*S */
-  int held_tiles;            /* two-shot: reduced tiles per lane each workgroup keeps in LDS across the
-                                barrier instead of storing and re-reading them (its whole share, 16 to
-                                40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
+  int held_tiles;            /* two-shot, R >= 6: reduced tiles per lane each workgroup keeps in LDS
+                                across the barrier instead of storing and re-reading them (its whole
+                                share, 16 to 40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
                                 turns it off, and the slicing below with it */
   int slices;                /* kernel launches the call runs as: 1, or, for a two-shot too large for its
                                 shares to fit in LDS, consecutive slices of slice_elems elements (the

@@ -446,9 +446,9 @@ def test_put_policies_at_the_cache_bound(algo):
             G.assert_matches_oracle(outs, want, dtype, f"{algo} n={n} in_place={in_place}")
 
 
-@pytest.mark.parametrize("R,n", [(8, 8 << 20), (8, 12_000_007), (16, 8 << 20), (5, 9_000_001), (7, 10_000_003),
+@pytest.mark.parametrize("R,n", [(8, 8 << 20), (8, 12_000_007), (16, 8 << 20), (6, 9_000_001), (7, 10_000_003),
                                  (12, 8_000_009)],
-                         ids=["r8_16MiB", "r8_ragged_24MB", "r16_16MiB", "r5_ragged", "r7_ragged", "r12_ragged"])
+                         ids=["r8_16MiB", "r8_ragged_24MB", "r16_16MiB", "r6_ragged", "r7_ragged", "r12_ragged"])
 def test_two_shot_held_in_lds(R, n):
     """The two-shot that keeps each workgroup's reduced tiles in LDS across
     the barrier (16 to 40 full tiles per workgroup), bf16, out of place and in
@@ -466,8 +466,8 @@ def test_two_shot_held_in_lds(R, n):
         G.assert_matches_oracle(outs, want, dtype, f"two_shot held R={R} n={n} in_place={in_place}")
 
 
-@pytest.mark.parametrize("R,n", [(8, 24_000_017), (16, 22_000_001), (5, 30_000_007)],
-                         ids=["r8_ragged_48MB", "r16_ragged_44MB", "r5_ragged_60MB"])
+@pytest.mark.parametrize("R,n", [(8, 24_000_017), (16, 22_000_001), (6, 30_000_007)],
+                         ids=["r8_ragged_48MB", "r16_ragged_44MB", "r6_ragged_60MB"])
 def test_two_shot_in_held_slices(R, n):
     """A two-shot too large for its shares to fit in LDS runs as consecutive
     tile-aligned slices, each a complete held two-shot; the last slice is
@@ -486,6 +486,9 @@ def test_two_shot_in_held_slices(R, n):
 
 
 def test_plan_geometry():
+    # no LDS hold below R = 6
+    r5 = M.channel_plan(G.channel(5), 30_000_007, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert r5.held_tiles == 0 and r5.slices == 1
     h = G.channel(8)
     p = M.channel_plan(h, W.prefill_bf16().count, M.BFLOAT16, M.ALGO_AUTO)
     assert p.algo == M.ALGO_TWO_SHOT and p.uses_barrier == 1 and p.threads_per_workgroup == 256
