@@ -191,6 +191,10 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * as consecutive slices of every buffer, each a complete two-shot on its own
  * element range, launched back to back on `stream` (mscl_channel_plan
  * reports the slices); the result is the same, as the sum is elementwise.
+ * That held two-shot uses all of each compute unit's LDS, one workgroup per
+ * compute unit; LDS-heavy kernels running at the same time on other streams
+ * can delay its workgroups past the wait bound (TIMEOUT is then recorded);
+ * MSCL_TWO_SHOT_HOLD=0 (environment, read once) avoids it.
  * Cache policy of the two-shot kernels' puts: when the call's footprint
  * (R inputs + R outputs, 2*R*count*element size) is at most 128 MiB they
  * are device-scope temporal stores, which leave the outputs in the
