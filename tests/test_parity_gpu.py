@@ -528,6 +528,11 @@ def test_plan_geometry():
     assert q.cached_puts == 1 and q.held_tiles == 0  # 8 tiles per workgroup: too few to hold
     for algo in (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_PORT):  # not a put policy of theirs
         assert M.channel_plan(h, mib8, M.BFLOAT16, algo).cached_puts == 0
+    # large chunks are whole 4 KiB pages even when n / R is not; small ones whole 16-byte vectors
+    q = M.channel_plan(h, 12_582_976, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.chunk_elems % 2048 == 0 and q.chunk_elems * 8 >= 12_582_976 and q.chunk_elems * 7 < 12_582_976
+    q = M.channel_plan(h, 100_003, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.chunk_elems == 12_504
     r16 = M.channel_plan(G.channel(16), W.ragged_outliers_bf16().count, M.BFLOAT16, M.ALGO_TWO_SHOT)
     assert r16.held_tiles == 32
     assert r16.chunk_elems % 8 == 0 and r16.chunk_elems * 16 >= W.ragged_outliers_bf16().count
