@@ -18,6 +18,10 @@
 //                       inputs into its own output), an arrival-only
 //                       barrier, all-gather (rank r puts its chunk into every
 //                       peer's output).
+//   mscl_twoshot_held   the two-shot with each workgroup's reduced tiles kept
+//                       in LDS across the barrier (no store and re-read of
+//                       the rank's chunk); the host runs large calls as
+//                       consecutive slices of it.
 //   mscl_twoshot_fused  reduce-scatter whose result goes from registers
 //                       straight into every output; no barrier.
 //   mscl_reduce_scatter_kernel / mscl_allgather_kernel
