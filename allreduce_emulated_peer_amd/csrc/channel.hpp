@@ -60,7 +60,7 @@ struct ChannelArgs {
 };
 
 // What a barrier orders across ranks (see RankChannels::barrier_all).
-enum class Sync { kPublish, kAfterReads, kArrival };
+enum class Sync { kPublish, kAfterReads, kAfterWrites, kArrival };
 
 // The channels of rank `rank`'s slot `slot` to all of its peers.
 struct RankChannels {
@@ -130,6 +130,17 @@ struct RankChannels {
   // skips kPublish's L2 write-back and invalidate, which on MI355X also
   // discard the L2 lines every rank is re-reading.
   //
+  // Sync::kAfterWrites is the completion barrier of puts made with
+  // device-scope stores (store_vec_scoped): every thread waits until its own
+  // stores have been acknowledged, which for device-scope stores means every
+  // XCD can see them, so the arrival-only signal that follows already carries
+  // the pages' promise that earlier writes are complete, without the L2
+  // write-back of a release fence.  Nothing is acquired after the waits: the
+  // kernels that end with this barrier read nothing afterwards, and the next
+  // kernel on the stream starts with invalidated caches.  (A consumer fused
+  // behind it in the same kernel would add an agent-scope acquire, an L2
+  // invalidate that measured 1.3-3 us per call on MI355X.)
+  //
   // Sync::kArrival is a pure rendezvous (arrival-only signal, no waiting for
   // earlier accesses, no acquire) for protocols in which no memory is shared
   // across ranks at this point; on MI355X it saves the per-workgroup L2
@@ -137,8 +148,9 @@ struct RankChannels {
   template <Sync kSync>
   __device__ void barrier_all() const {
     constexpr bool kPublishing = kSync == Sync::kPublish;
+    constexpr bool kCompleting = kSync == Sync::kAfterReads || kSync == Sync::kAfterWrites;
     if (kPublishing) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's accesses, published
-    if (kSync == Sync::kAfterReads) __builtin_amdgcn_s_waitcnt(0);  // this thread's accesses, completed
+    if (kCompleting) __builtin_amdgcn_s_waitcnt(0);  // this thread's accesses, completed
     __syncthreads();  // every local thread has reached the barrier
     if (threadIdx.x < 64) {
       const int peer = threadIdx.x;

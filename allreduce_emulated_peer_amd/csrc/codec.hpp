@@ -137,6 +137,43 @@ __device__ inline void store_vec_device(void* base, uint32_t nbytes, uint64_t vi
   __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, static_cast<uint32_t>(vi * 16), 0, kBufferSc1);
 }
 
+// Device-scope puts addressed from a wave-uniform base: a buffer resource
+// starts at vector `v0` of `base` and covers `nvec` vectors, so every offset
+// fits 32 bits whatever the buffer's size, and a lane whose vector lies past
+// the range has its store dropped by the hardware's range check.  kCpol is
+// the cache-policy operand: kBufferSc1 (device scope, temporal) or
+// kBufferSc1 | kBufferNt (device scope, streaming).  A store with device
+// scope is acknowledged only once every XCD can see it, so waiting for the
+// acknowledgement (s_waitcnt) is all a later signal needs to publish it: the
+// whole-L2 write-back of a release fence is not needed for these stores.
+constexpr int kBufferNt = 1 << 1;  // cache-policy operand: nt
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(void* base, uint64_t v0, uint64_t nvec) {
+  return __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(base) + v0 * 16, 0, static_cast<int>(nvec * 16),
+                                           kRawBufferWord3);
+}
+template <int kCpol>
+__device__ inline void store_vec_scoped(__amdgpu_buffer_rsrc_t rsrc, uint32_t vi, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, vi * 16, 0, kCpol);
+}
+
+// The first `nvalid` (< V) elements of vector `vi` of `base`, stored element
+// by element with device scope (the partial vector at a buffer's end).
+template <class C, int kCpol>
+__device__ inline void store_partial_scoped(void* base, uint64_t vi, const u32x4& v, int nvalid) {
+  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(base, vi, 1);
+  if constexpr (C::kElemBytes == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nvalid) __builtin_amdgcn_raw_buffer_store_b32(v[k], rsrc, 4 * k, 0, kCpol);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nvalid)
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v[k >> 1] >> (16 * (k & 1))), rsrc, 2 * k, 0,
+                                              kCpol);
+  }
+}
+
 // First `nvalid` (< V) elements of vector `vi`; the rest read as zero bits.
 template <class C>
 __device__ inline u32x4 load_partial(const void* base, uint64_t vi, int nvalid) {

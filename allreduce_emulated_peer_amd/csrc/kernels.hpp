@@ -23,7 +23,9 @@
 //                       the rank's chunk); the host runs large calls as
 //                       consecutive slices of it.
 //   mscl_twoshot_fused  reduce-scatter whose result goes from registers
-//                       straight into every output; no barrier.
+//                       straight into every output as device-scope puts,
+//                       then a completion barrier (or, as an explicitly
+//                       requested variant, no barrier).
 //   mscl_reduce_scatter_kernel / mscl_allgather_kernel
 //                       the two halves as standard collectives.
 //   mscl_channel_selftest_kernel
@@ -536,23 +538,48 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_port(KernelArgs a) {
 // tile of chunk r and writes the rounded vector straight into every rank's
 // output (its own included), so the reduced chunk is never re-read and the
 // call moves exactly R*S bytes in and R*S out.  Inputs are read once and
-// outputs written once, so both stream past the caches.  No barrier runs
-// inside the call: rank r writes only chunk r of every output, which no
-// other rank reads or writes during the call, and in place the only reader
-// of in[p][chunk r] is rank r itself, each lane loading a vector from every
-// input before it stores that vector.
+// stream past the caches.  Rank r writes only chunk r of every output, which
+// no other rank reads or writes during the call, and in place the only
+// reader of in[p][chunk r] is rank r itself, each lane loading a vector from
+// every input before it stores that vector; so no barrier is needed between
+// the reduction and the puts.
+//
+// kComplete: the call ends with the method's completion barrier.  The puts
+// are device-scope stores (store_vec_scoped), and each workgroup, once its
+// puts are acknowledged, signals the same slot of every peer ("my puts into
+// your output are done") and waits for theirs (Sync::kAfterWrites); a
+// workgroup leaves the kernel only when every rank has finished putting its
+// slot's tiles into this rank's output.  Measured on MI355X (R = 8 bf16,
+// graph replay, us, with -> without the barrier): 512 KiB 3.8 -> 2.5, 2 MiB
+// 5.6 -> 4.3, 8 MiB 21.0 -> 19.6.  Without kComplete (an explicitly requested
+// variant) completion is the end of the kernel on the stream, which on one
+// GPU covers every rank at once.
 template <class C, int R, int U, bool kFull, int T, Put kP>
 __device__ inline void put_all_tile(const KernelArgs& a, const u32x4 (&y)[U], uint64_t base, uint64_t vend) {
 #pragma unroll
   for (int p = 0; p < R; ++p) store_tile<U, kFull, kP, T>(a.out[p], y, base, vend);
 }
 
+// The same puts as device-scope stores: tile base `v0` (wave-uniform), `nvec`
+// vectors in the tile's range, lane `lane` writing vectors lane, lane + T, ...
+template <int R, int U, int T, int kCpol>
+__device__ inline void put_all_tile_scoped(const KernelArgs& a, const u32x4 (&y)[U], uint64_t v0, uint64_t nvec,
+                                           uint32_t lane) {
+#pragma unroll
+  for (int p = 0; p < R; ++p) {
+    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(a.out[p], v0, nvec);
+#pragma unroll
+    for (int u = 0; u < U; ++u) store_vec_scoped<kCpol>(rsrc, lane + static_cast<uint32_t>(u * T), y[u]);
+  }
+}
+
 // T threads per workgroup: 256, or 128 for messages too small to give every
 // CU one 256-lane tile (more, smaller workgroups spread the loads).
-template <class C, int R, int T, bool kCachedPuts>
+template <class C, int R, int T, bool kCachedPuts, bool kComplete>
 __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
   constexpr int V = C::V;
   constexpr Put kP = put_policy<kCachedPuts>();
+  constexpr int kCpol = kCachedPuts ? kBufferSc1 : (kBufferSc1 | kBufferNt);
   constexpr int U = unroll_for<R>();
   constexpr uint64_t kTile = static_cast<uint64_t>(T) * U;
   const int rank = blockIdx.x % R;
@@ -580,7 +607,10 @@ __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
       if (more) load_tile<R, U, true, true, T>(nxt, a.in, lane_base + tn * kTile, v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
-      put_all_tile<C, R, U, true, T, kP>(a, y, lane_base + t * kTile, v_full);
+      if constexpr (kComplete)
+        put_all_tile_scoped<R, U, T, kCpol>(a, y, v_lo + t * kTile, kTile, threadIdx.x);
+      else
+        put_all_tile<C, R, U, true, T, kP>(a, y, lane_base + t * kTile, v_full);
       if (!more) break;
       for (int u = 0; u < U; ++u)
         for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
@@ -593,19 +623,28 @@ __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
     const uint64_t base = lane_base + nfull_tiles * kTile;
     load_tile<R, U, false, true, T>(x, a.in, base, v_full);
     reduce_tile<C, R, U>(y, x);
-    put_all_tile<C, R, U, false, T, kP>(a, y, base, v_full);
+    if constexpr (kComplete) {
+      const uint64_t v0 = v_lo + nfull_tiles * kTile;
+      put_all_tile_scoped<R, U, T, kCpol>(a, y, v0, v_full - v0, threadIdx.x);  // lanes past v_full dropped
+    } else {
+      put_all_tile<C, R, U, false, T, kP>(a, y, base, v_full);
+    }
   }
   if (ntail != 0 && slot == 0 && threadIdx.x == 0) {
     const u32x4 y = reduce_partial<C, R>(a, v_full, ntail);
 #pragma unroll
-    for (int p = 0; p < R; ++p) store_partial<C>(a.out[p], v_full, y, ntail);
+    for (int p = 0; p < R; ++p) {
+      if constexpr (kComplete)
+        store_partial_scoped<C, kBufferSc1>(a.out[p], v_full, y, ntail);
+      else
+        store_partial<C>(a.out[p], v_full, y, ntail);
+    }
   }
 
-  // Completion is the end of the kernel on the stream: nothing inside the
-  // call reads the outputs.  (Across GPUs this is where each rank would
-  // signal "my puts into your output are done" and wait for its peers'; on
-  // one GPU an in-kernel ordered handshake measured 20-30 us per call for no
-  // observer.)
+  if constexpr (kComplete) {
+    const RankChannels chans{a.ch, R, rank, slot};
+    chans.template barrier_all<Sync::kAfterWrites>();
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -828,7 +867,13 @@ enum {
   kAlgoTwoShotCachedPuts = 10,
   kAlgoTwoShotFusedCachedPuts = 11,
   kAlgoTwoShotFusedHalfCachedPuts = 12,
-  kAlgoTwoShotHeld = 13  // the two-shot keeping reduced tiles in LDS (mscl_twoshot_held)
+  kAlgoTwoShotHeld = 13,  // the two-shot keeping reduced tiles in LDS (mscl_twoshot_held)
+  // the fused two-shot with its completion barrier (the kinds above run it
+  // without): 256 / 128 threads, streaming / device-scope temporal puts
+  kAlgoTwoShotFusedSync = 14,
+  kAlgoTwoShotFusedHalfSync = 15,
+  kAlgoTwoShotFusedCachedPutsSync = 16,
+  kAlgoTwoShotFusedHalfCachedPutsSync = 17
 };
 
 template <class C, int R>
@@ -837,11 +882,15 @@ constexpr KernelFn kernel_for(int kind) {
     case kAlgoOneShot: return &mscl_oneshot<C, R, false>;
     case kAlgoOneShotInPlace: return &mscl_oneshot<C, R, true>;
     case kAlgoTwoShot: return &mscl_twoshot<C, R, false>;
-    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R, kThreads, false>;
-    case kAlgoTwoShotFusedHalf: return &mscl_twoshot_fused<C, R, kThreads / 2, false>;
+    case kAlgoTwoShotFused: return &mscl_twoshot_fused<C, R, kThreads, false, false>;
+    case kAlgoTwoShotFusedHalf: return &mscl_twoshot_fused<C, R, kThreads / 2, false, false>;
     case kAlgoTwoShotCachedPuts: return &mscl_twoshot<C, R, true>;
-    case kAlgoTwoShotFusedCachedPuts: return &mscl_twoshot_fused<C, R, kThreads, true>;
-    case kAlgoTwoShotFusedHalfCachedPuts: return &mscl_twoshot_fused<C, R, kThreads / 2, true>;
+    case kAlgoTwoShotFusedCachedPuts: return &mscl_twoshot_fused<C, R, kThreads, true, false>;
+    case kAlgoTwoShotFusedHalfCachedPuts: return &mscl_twoshot_fused<C, R, kThreads / 2, true, false>;
+    case kAlgoTwoShotFusedSync: return &mscl_twoshot_fused<C, R, kThreads, false, true>;
+    case kAlgoTwoShotFusedHalfSync: return &mscl_twoshot_fused<C, R, kThreads / 2, false, true>;
+    case kAlgoTwoShotFusedCachedPutsSync: return &mscl_twoshot_fused<C, R, kThreads, true, true>;
+    case kAlgoTwoShotFusedHalfCachedPutsSync: return &mscl_twoshot_fused<C, R, kThreads / 2, true, true>;
     case kAlgoTwoShotHeld: return &mscl_twoshot_held<C, R>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
@@ -872,7 +921,10 @@ inline KernelFn kernel_lookup(int kind, int dtype, int R) {
 inline int unroll_for_runtime(int R) { return R <= 2 ? 4 : (R <= 4 ? 2 : 1); }
 
 inline int threads_for_kind(int kind) {
-  return (kind == kAlgoTwoShotFusedHalf || kind == kAlgoTwoShotFusedHalfCachedPuts) ? kThreads / 2 : kThreads;
+  return (kind == kAlgoTwoShotFusedHalf || kind == kAlgoTwoShotFusedHalfCachedPuts || kind == kAlgoTwoShotFusedHalfSync ||
+          kind == kAlgoTwoShotFusedHalfCachedPutsSync)
+             ? kThreads / 2
+             : kThreads;
 }
 
 }  // namespace mscl

@@ -42,7 +42,11 @@ size_t elem_bytes(int dtype) { return dtype == MSCL_FLOAT32 ? 4 : 2; }
 
 bool valid_algo(int algo) {
   return algo == MSCL_ALGO_AUTO || algo == MSCL_ALGO_ONE_SHOT || algo == MSCL_ALGO_TWO_SHOT ||
-         algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_PORT;
+         algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_PORT ||
+         algo == MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER;
+}
+
+bool is_fused(int algo) { return algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER;
 }
 
 size_t env_size(const char* name, size_t dflt) {
@@ -164,57 +168,55 @@ mscl_status_t validate_call(const void* const inputs[], void* const outputs[], s
   return MSCL_SUCCESS;
 }
 
-// AUTO's size bands, from device time per call on MI355X with bf16 buffers
-// (small sizes replayed from a graph, large ones timed over back-to-back calls):
-//   one-shot        up to oneshot_max_bytes(R): 64 MiB at R <= 2, 512 KiB at
-//                   R <= 4, 128 KiB at R <= 8, 64 KiB above (it reads R*S per
-//                   rank, from cache while the buffers fit: R = 2 out of place,
-//                   64 MiB 40.4 us against 44.9 fused, 80 MiB 75.1 against 56.1);
-//   fused two-shot  up to fused_max_bytes(R): no barrier and no re-read, best in
-//                   the middle (R = 8, 1 MiB: 3.7 us against 5.2 two-shot, 6.4
-//                   one-shot) and, with few ranks, at every size;
+// AUTO's size bands (bytes per rank buffer), from device time per call on
+// MI355X, bf16, calls replayed from a graph, over the same buffers ("hot")
+// and over buffer sets rotated past the 256 MB Infinity Cache ("cold"); a
+// band goes to the algorithm with the smaller hot + cold sum.  Every
+// algorithm AUTO picks carries the method's synchronisation: the one-shot
+// needs none, the two-shot runs its barrier between reduce-scatter and
+// all-gather, the fused two-shot its completion barrier.
+//   one-shot        up to oneshot_max_bytes(R): it reads R*S per rank, from
+//                   cache while the buffers fit, and has no barrier (R = 8,
+//                   256 KiB: 2.8 / 3.8 us against 3.6 / 4.4 fused; 512 KiB:
+//                   4.2 / 6.5 against 3.9 / 5.0);
+//   fused two-shot  up to fused_max_bytes(R): no re-read, one barrier at the
+//                   end (R = 8, 2 MiB: 5.7 / 8.9 against 6.2 / 8.7 two-shot);
+//                   with few ranks at every size (R = 3, 128 MiB: 145 against
+//                   149);
 //   two-shot        above: its separate read and write phases stream HBM best
-//                   with many ranks (R = 8, 128 MiB: 376 us against 381 fused).
-// In place, the one-shot needs a barrier between each batch of tiles' loads
-// and stores (a rank overwrites an input its peers still read: R = 8,
-// 512 KiB, 7.3 us), while the fused two-shot needs none (2.9 us), so
-// in-place calls skip the first band.
+//                   with many ranks (R = 8, 4 MiB 11.3 / 15.4 against
+//                   12.4 / 15.0; 128 MiB 356 against 405 fused).
+// In place the one-shot needs a barrier between each batch of tiles' loads
+// and stores (a rank overwrites an input its peers still read), so in-place
+// calls skip the first band; the fused band is then wider at R = 5 and 8
+// (R = 8 in place, 8 MiB: 21.1 / 20.9 against 22.5 / 25.6).
 size_t oneshot_max_bytes(int nranks) {
   const size_t env = config().oneshot_max_bytes;
   if (env != SIZE_MAX) return env;
-  if (nranks <= 2) return size_t(64) << 20;
-  if (nranks <= 4) return size_t(512) << 10;
-  if (nranks <= 8) return size_t(128) << 10;
-  return size_t(64) << 10;
+  if (nranks <= 2) return size_t(8) << 20;  // R = 2, 8 MiB: 5.5 / 10.0 against 5.8 / 9.6 fused
+  if (nranks == 3) return size_t(2) << 20;
+  if (nranks <= 5) return size_t(1) << 20;  // R = 4, 2 MiB: 4.7 / 8.3 against 4.4 / 5.8 fused
+  if (nranks <= 7) return size_t(512) << 10;
+  if (nranks <= 11) return size_t(256) << 10;
+  return size_t(128) << 10;  // R = 16, 256 KiB: 5.8 / 8.8 against 5.4 / 6.2 fused
 }
 
 // Up to this many bytes per rank buffer the fused two-shot also gets two
 // workgroups per compute unit (make_plan).
 constexpr size_t kFusedMaxBytes = size_t(4) << 20;
 
-// The fused two-shot's upper bound in AUTO.  With few ranks it beats the
-// two-shot at every size measured (128 MiB: R = 2 85.8 us against 96.7 in
-// place, 89.4 against 97.5 out of place; R = 5 in place 271 against 292); out
-// of place at R = 3, 4 and 6 the two-shot catches up at 128, 64 and 32 MiB
-// (R = 4, 128 MiB: 189.5 against 182.6); from R = 7 on it is ahead above
-// 4 MiB (R = 7 in place, 32 MiB: 105.0 against 113.2).  Up to 8 MiB at R = 7
-// and 8, and 16 MiB at R = 6, the fused kernel stays in front, with its
-// device-scope puts (cached_puts) below 128 MiB of footprint: R = 8, 8 MiB,
-// 20.4 against 20.8 us with cached buffers, 24.9 against 26.4 with uncached
-// ones, 13.8 against 15.2 between a producer and a consumer kernel; R = 7,
-// 8 MiB, 23.4 / 31.3 / 19.9 against 23.4 / 38.9 / 21.1; R = 6, 16 MiB,
-// 44.6 / 42.7 / 43.3 against 44.2 / 43.4 / 48.0.
+// The fused two-shot's upper bound in AUTO (see above).
 size_t fused_max_bytes(int nranks, bool in_place) {
-  if (nranks <= 2 || (in_place && nranks <= 6)) return SIZE_MAX;
   switch (nranks) {
-    case 3: return size_t(96) << 20;
-    case 4: return size_t(32) << 20;
-    case 5: return SIZE_MAX;
-    case 6: return size_t(16) << 20;
-    case 7:
-    case 8: return size_t(8) << 20;
+    case 1:
+    case 2:
+    case 3: return SIZE_MAX;
+    case 4: return size_t(16) << 20;  // 32 MiB: 49.5 / 51.4 against 48.5 / 48.3 two-shot
+    case 5: return in_place ? SIZE_MAX : size_t(8) << 20;
+    case 8: return size_t(in_place ? 8 : 2) << 20;
+    case 16: return size_t(256) << 10;  // 512 KiB: 7.1 / 8.2 against 6.3 / 7.7 two-shot
   }
-  return kFusedMaxBytes;
+  return size_t(1) << 20;  // R = 6, 7, 9..15; R = 12, 2 MiB: 14.0 / 15.0 against 10.0 / 13.0 two-shot
 }
 
 mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo, bool in_place) {
@@ -245,8 +247,8 @@ constexpr size_t kCachedPutsMaxFootprint = size_t(128) << 20;
 // 49.0 us; R = 8, 16 MiB, 16 tiles, 44.3 -> 43.3 us).
 constexpr uint64_t kHeldMinTiles = 16;
 bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
-  if (algo != MSCL_ALGO_TWO_SHOT && algo != MSCL_ALGO_TWO_SHOT_FUSED) return false;
-  if (bytes > (size_t(1) << 31)) return false;  // the buffer store's 32-bit byte range
+  if (algo != MSCL_ALGO_TWO_SHOT && !is_fused(algo)) return false;
+  if (bytes > (size_t(1) << 31)) return false;  // the two-shot's buffer store takes a 32-bit byte range
   const size_t env = config().cached_puts_max_footprint;
   const size_t limit = env != SIZE_MAX ? env : kCachedPutsMaxFootprint;
   return 2 * static_cast<size_t>(nranks) * bytes <= limit;
@@ -265,7 +267,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   plan->vectors_per_thread = unroll_for_runtime(R);
   plan->cached_puts = cached_puts(algo, R, count * elem_bytes(dtype)) ? 1 : 0;
   uint64_t vectors;  // full vectors one rank covers
-  if (algo == MSCL_ALGO_TWO_SHOT || algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_PORT) {
+  if (algo == MSCL_ALGO_TWO_SHOT || is_fused(algo) || algo == MSCL_ALGO_TWO_SHOT_PORT) {
     const uint64_t per = (count + R - 1) / R;
     // Chunks are whole 16-byte vectors; from 32 pages of 4 KiB per rank up,
     // whole 4 KiB pages, so that every rank's chunk starts where its tiles
@@ -279,7 +281,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
     const uint64_t c = (per + align - 1) / align * align;
     plan->chunk_elems = c;
     vectors = c / V;
-    plan->uses_barrier = algo == MSCL_ALGO_TWO_SHOT ? 1 : 0;
+    plan->uses_barrier = (algo == MSCL_ALGO_TWO_SHOT || algo == MSCL_ALGO_TWO_SHOT_FUSED) ? 1 : 0;
   } else {
     vectors = count / V;
     plan->uses_barrier = in_place ? 1 : 0;
@@ -290,7 +292,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   // two-shot takes two in AUTO's middle band, up to kFusedMaxBytes per rank,
   // where a rank's chunk is only a few tiles per workgroup (R = 8 bf16, 4 MiB:
   // 12.2 -> 10.3 us); above it two are slower (128 MiB: 390 -> 401 us).
-  const bool fused_band = algo == MSCL_ALGO_TWO_SHOT_FUSED && count * elem_bytes(dtype) <= kFusedMaxBytes;
+  const bool fused_band = is_fused(algo) && count * elem_bytes(dtype) <= kFusedMaxBytes;
   const uint64_t per_cu = fused_band ? 2 : 1;
   const uint64_t total = cfg.wg_target_total ? cfg.wg_target_total : static_cast<uint64_t>(ch->cus) * per_cu;
   uint64_t cap = cfg.wg_per_rank ? cfg.wg_per_rank : std::max<uint64_t>(1, total / R);
@@ -479,6 +481,88 @@ uint32_t blocks_for(const mscl_channel_s* ch, size_t count, int dtype, int nrank
   return static_cast<uint32_t>(std::min(want, cap));
 }
 
+// Barrier slots for `nranks` ranks on the current device: the fewest
+// workgroups per rank that can be resident at once over every kernel that runs
+// a barrier (so a barrier never waits on a workgroup that has not been
+// scheduled), and the same bound for the held two-shot, whose 160 KiB of LDS
+// leaves room for one workgroup per compute unit (kept apart so that the other
+// kernels keep theirs).
+hipError_t barrier_slots(int nranks, int cus, uint32_t* slots, uint32_t* held_slots) {
+  int min_resident = 1 << 30;
+  for (int dt = 0; dt < 3; ++dt) {
+    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot, kAlgoTwoShotCachedPuts, kAlgoTwoShotFusedSync,
+                     kAlgoTwoShotFusedCachedPutsSync, kAlgoTwoShotFusedHalfSync, kAlgoTwoShotFusedHalfCachedPutsSync}) {
+      int per_cu = 0;
+      const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)), threads_for_kind(kind), 0);
+      if (e != hipSuccess) return e;
+      min_resident = std::min(min_resident, per_cu * cus);
+    }
+  }
+  *slots = static_cast<uint32_t>(std::max(1, std::min(min_resident / nranks, 4096)));
+  int held_resident = 1 << 30;
+  for (int dt = 0; dt < 3; ++dt) {
+    int per_cu = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(kernel_lookup(kAlgoTwoShotHeld, dt, nranks)), kThreads, 0);
+    if (e != hipSuccess) return e;
+    held_resident = std::min(held_resident, per_cu * cus);
+  }
+  *held_slots = static_cast<uint32_t>(std::min<int>(held_resident / nranks, static_cast<int>(*slots)));
+  return hipSuccess;
+}
+
+// The kernel kind a planned call (or slice) launches.
+int kind_for(const mscl_plan_t& plan, bool in_place) {
+  const bool cached = plan.cached_puts != 0;
+  const bool wide = plan.threads_per_workgroup == kThreads;
+  switch (plan.algo) {
+    case MSCL_ALGO_TWO_SHOT:
+      return plan.held_tiles ? kAlgoTwoShotHeld : cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot;
+    case MSCL_ALGO_TWO_SHOT_FUSED:
+      return wide ? (cached ? kAlgoTwoShotFusedCachedPutsSync : kAlgoTwoShotFusedSync)
+                  : (cached ? kAlgoTwoShotFusedHalfCachedPutsSync : kAlgoTwoShotFusedHalfSync);
+    case MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER:
+      return wide ? (cached ? kAlgoTwoShotFusedCachedPuts : kAlgoTwoShotFused)
+                  : (cached ? kAlgoTwoShotFusedHalfCachedPuts : kAlgoTwoShotFusedHalf);
+    case MSCL_ALGO_TWO_SHOT_PORT:
+      return kAlgoTwoShotPort;
+    default:
+      return in_place ? kAlgoOneShotInPlace : kAlgoOneShot;
+  }
+}
+
+// Launch a validated AllReduce as planned on `ch`'s geometry: one kernel, or
+// one per slice for a sliced two-shot (each slice a complete two-shot on its
+// own element range, planned on its own; an AllReduce is elementwise, so the
+// result is the same), in stream order.  `proto` carries the channel state
+// (and port arguments) every launch uses.
+mscl_status_t launch_allreduce(const mscl_channel_s* ch, const KernelArgs& proto, const void* const inputs[],
+                               void* const outputs[], size_t count, int dtype, int nranks, mscl_algo_t resolved,
+                               bool in_place, void* stream) {
+  mscl_plan_t plan;
+  make_plan(ch, count, dtype, resolved, in_place, &plan);
+  const size_t e = elem_bytes(dtype);
+  const size_t step = plan.slices > 1 ? plan.slice_elems : count;
+  for (size_t lo = 0; lo < count; lo += step) {
+    const size_t c = std::min(step, count - lo);
+    KernelArgs a = proto;
+    for (int r = 0; r < nranks; ++r) {
+      a.in[r] = static_cast<const char*>(inputs[r]) + lo * e;
+      a.out[r] = static_cast<char*>(outputs[r]) + lo * e;
+    }
+    a.count = c;
+    mscl_plan_t sp = plan;
+    if (plan.slices > 1) make_plan(ch, c, dtype, resolved, in_place, &sp, /*allow_slices=*/false);
+    a.chunk = sp.chunk_elems;
+    a.nblk = static_cast<uint32_t>(sp.workgroups_per_rank);
+    a.xcd_grouped = (resolved == MSCL_ALGO_ONE_SHOT && a.nblk % kXcds == 0) ? 1u : 0u;
+    if (const mscl_status_t st = launch(kind_for(sp, in_place), dtype, nranks, a, stream); st != MSCL_SUCCESS)
+      return st;
+  }
+  return MSCL_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -547,39 +631,12 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
     ch->wall_clock_khz = static_cast<uint64_t>(khz);
-  // Slots: the fewest workgroups per rank that can be resident at once over
-  // every kernel that runs the barrier, so a barrier can never wait on a
-  // workgroup that has not been scheduled.
-  int min_resident = 1 << 30;
-  for (int dt = 0; dt < 3; ++dt) {
-    for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot, kAlgoTwoShotCachedPuts}) {
-      int per_cu = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)),
-                                                       kThreads, 0);
-      if (e != hipSuccess) {
-        delete ch;
-        (void)hipSetDevice(prev);
-        return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-      }
-      min_resident = std::min(min_resident, per_cu * ch->cus);
-    }
+  e = barrier_slots(nranks, ch->cus, &ch->slots, &ch->held_slots);
+  if (e != hipSuccess) {
+    delete ch;
+    (void)hipSetDevice(prev);
+    return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   }
-  ch->slots = static_cast<uint32_t>(std::max(1, std::min(min_resident / nranks, 4096)));
-  // The held two-shot's 160 KiB of LDS leaves room for one workgroup per
-  // compute unit; it gets its own bound so that the other kernels keep theirs.
-  int held_resident = 1 << 30;
-  for (int dt = 0; dt < 3; ++dt) {
-    int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(kernel_lookup(kAlgoTwoShotHeld, dt, nranks)), kThreads, 0);
-    if (e != hipSuccess) {
-      delete ch;
-      (void)hipSetDevice(prev);
-      return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    }
-    held_resident = std::min(held_resident, per_cu * ch->cus);
-  }
-  ch->held_slots = static_cast<uint32_t>(std::min<int>(held_resident / nranks, static_cast<int>(ch->slots)));
   const size_t inbound_bytes = sizeof(uint32_t) * nranks * nranks * ch->slots;
   const size_t consumed_bytes = sizeof(uint32_t) * nranks * ch->slots;
   mscl_status_t st = MSCL_SUCCESS;
@@ -686,14 +743,8 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
   if ((st = bind_channel(nranks, &b)) != MSCL_SUCCESS) return st;
 
   const mscl_algo_t resolved = resolve_algo(count, dtype, nranks, algo, in_place);
-  mscl_plan_t plan;
-  make_plan(b.ch, count, dtype, resolved, in_place, &plan);
-
   KernelArgs a;
   fill_args(&a, b, inputs, outputs, nranks, count);
-  a.chunk = plan.chunk_elems;
-  a.nblk = static_cast<uint32_t>(plan.workgroups_per_rank);
-  a.xcd_grouped = (resolved == MSCL_ALGO_ONE_SHOT && a.nblk % kXcds == 0) ? 1u : 0u;
   if (resolved == MSCL_ALGO_TWO_SHOT_PORT) {
     std::lock_guard<std::mutex> lock(g_mutex);
     if ((st = port_start(b.ch)) != MSCL_SUCCESS) return st;
@@ -705,41 +756,7 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
     a.port.arrived = ps->arrived;
     a.port.fifo_mask = proxy::PortState::kEntries - 1;
   }
-  if (plan.slices > 1) {
-    // Consecutive slices, each a complete two-shot on its own element range
-    // (an AllReduce is elementwise, so the result is the same), planned and
-    // launched in stream order on the same channel set.
-    const size_t e = elem_bytes(dtype);
-    for (size_t lo = 0; lo < count; lo += plan.slice_elems) {
-      const size_t c = std::min(plan.slice_elems, count - lo);
-      const void* sin[kMaxRanks];
-      void* sout[kMaxRanks];
-      for (int r = 0; r < nranks; ++r) {
-        sin[r] = static_cast<const char*>(inputs[r]) + lo * e;
-        sout[r] = static_cast<char*>(outputs[r]) + lo * e;
-      }
-      mscl_plan_t sp;
-      make_plan(b.ch, c, dtype, resolved, in_place, &sp, /*allow_slices=*/false);
-      KernelArgs sa;
-      fill_args(&sa, b, sin, sout, nranks, c);
-      sa.chunk = sp.chunk_elems;
-      sa.nblk = static_cast<uint32_t>(sp.workgroups_per_rank);
-      const int kind = sp.held_tiles ? kAlgoTwoShotHeld : sp.cached_puts ? kAlgoTwoShotCachedPuts : kAlgoTwoShot;
-      if ((st = launch(kind, dtype, nranks, sa, stream)) != MSCL_SUCCESS) return st;
-    }
-    return MSCL_SUCCESS;
-  }
-  const bool cached = plan.cached_puts != 0;
-  const int kind = resolved == MSCL_ALGO_TWO_SHOT
-                       ? (plan.held_tiles ? kAlgoTwoShotHeld : cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot)
-                   : resolved == MSCL_ALGO_TWO_SHOT_FUSED
-                       ? (plan.threads_per_workgroup == kThreads
-                              ? (cached ? kAlgoTwoShotFusedCachedPuts : kAlgoTwoShotFused)
-                              : (cached ? kAlgoTwoShotFusedHalfCachedPuts : kAlgoTwoShotFusedHalf))
-                   : resolved == MSCL_ALGO_TWO_SHOT_PORT  ? kAlgoTwoShotPort
-                   : in_place                             ? kAlgoOneShotInPlace
-                                                          : kAlgoOneShot;
-  return launch(kind, dtype, nranks, a, stream);
+  return launch_allreduce(b.ch, a, inputs, outputs, count, dtype, nranks, resolved, in_place, stream);
 }
 
 mscl_status_t mscl_reduce_scatter(const void* const inputs[], void* const outputs[], size_t recvcount,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmscl.so")
 
 FLOAT32, FLOAT16, BFLOAT16 = 0, 1, 2
 ALGO_AUTO, ALGO_ONE_SHOT, ALGO_TWO_SHOT, ALGO_TWO_SHOT_FUSED, ALGO_TWO_SHOT_PORT = 0, 1, 2, 3, 4
+ALGO_TWO_SHOT_FUSED_NOBARRIER = 5
 MAX_RANKS = 16
 
 SUCCESS = 0
@@ -33,7 +34,8 @@ ERR_TIMEOUT = 7
 
 DTYPE_CODES = {"fp32": FLOAT32, "fp16": FLOAT16, "bf16": BFLOAT16}
 ALGO_CODES = {"auto": ALGO_AUTO, "one_shot": ALGO_ONE_SHOT, "two_shot": ALGO_TWO_SHOT,
-              "two_shot_fused": ALGO_TWO_SHOT_FUSED, "two_shot_port": ALGO_TWO_SHOT_PORT}
+              "two_shot_fused": ALGO_TWO_SHOT_FUSED, "two_shot_port": ALGO_TWO_SHOT_PORT,
+              "two_shot_fused_nobarrier": ALGO_TWO_SHOT_FUSED_NOBARRIER}
 
 # every function include/mscl.h declares
 EXPORTS = (
@@ -89,8 +91,9 @@ def load(path: str = LIB_PATH):
     for name in ("mscl_channel_destroy", "mscl_channel_check", "mscl_channel_reset"):
         getattr(lib, name).restype = c_int
         getattr(lib, name).argtypes = [vp]
-    lib.mscl_allreduce.restype = c_int
-    lib.mscl_allreduce.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, c_int, vp]
+    for name in ("mscl_allreduce",):
+        getattr(lib, name).restype = c_int
+        getattr(lib, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, c_int, vp]
     for name in ("mscl_reduce_scatter", "mscl_allgather"):
         getattr(lib, name).restype = c_int
         getattr(lib, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, vp]

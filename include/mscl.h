@@ -57,14 +57,20 @@ typedef enum {
   MSCL_ALGO_AUTO = 0,          /* by size: one-shot, then fused two-shot, then two-shot */
   MSCL_ALGO_ONE_SHOT = 1,      /* every rank reads all R inputs and writes its own output */
   MSCL_ALGO_TWO_SHOT = 2,      /* reduce-scatter, device signal/wait barrier, all-gather put */
-  MSCL_ALGO_TWO_SHOT_FUSED = 3, /* reduce-scatter whose all-gather put goes out from registers
-                                   (no re-read of the reduced chunk, no barrier inside the call;
-                                   completion is the end of the call on the stream) */
-  MSCL_ALGO_TWO_SHOT_PORT = 4   /* reduce-scatter in the kernel; the all-gather puts go through a
+  MSCL_ALGO_TWO_SHOT_FUSED = 3, /* reduce-scatter whose all-gather puts go out from registers
+                                   (no re-read of the reduced chunk), then the completion
+                                   barrier: each rank signals its peers once its puts into
+                                   their outputs are visible, and waits for theirs */
+  MSCL_ALGO_TWO_SHOT_PORT = 4,  /* reduce-scatter in the kernel; the all-gather puts go through a
                                    port channel: each rank's last workgroup posts R-1 put
                                    requests to a host proxy thread, which copies them with the
                                    SDMA engines, and waits for their completion.  Never chosen
                                    by AUTO (see mscl_allreduce) */
+  MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER = 5 /* MSCL_ALGO_TWO_SHOT_FUSED without the completion
+                                   barrier: no signal or wait at all; completion is the end of
+                                   the kernel on the stream, which covers every rank only
+                                   because all ranks share one GPU.  A comparison variant,
+                                   never chosen by AUTO */
 } mscl_algo_t;
 
 typedef int mscl_status_t;

@@ -20,8 +20,9 @@ from oracle import allreduce as O
 TORCH_DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 CODES = {"fp32": M.FLOAT32, "fp16": M.FLOAT16, "bf16": M.BFLOAT16}
 ALGOS = {"one_shot": M.ALGO_ONE_SHOT, "two_shot": M.ALGO_TWO_SHOT, "two_shot_fused": M.ALGO_TWO_SHOT_FUSED,
-         "two_shot_port": M.ALGO_TWO_SHOT_PORT, "auto": M.ALGO_AUTO}
-EXPLICIT = ("one_shot", "two_shot", "two_shot_fused", "two_shot_port")
+         "two_shot_port": M.ALGO_TWO_SHOT_PORT, "two_shot_fused_nobarrier": M.ALGO_TWO_SHOT_FUSED_NOBARRIER,
+         "auto": M.ALGO_AUTO}
+EXPLICIT = ("one_shot", "two_shot", "two_shot_fused", "two_shot_port", "two_shot_fused_nobarrier")
 POISON = 0xA5
 
 _channels = {}
@@ -60,8 +61,9 @@ def poison_like(t: torch.Tensor) -> torch.Tensor:
 
 
 def run(xs, dtype, algo="auto", in_place=False, stream=None, dev_inputs=None):
-    """Run the HIP AllReduce on host inputs; returns the device outputs."""
-    R = len(xs)
+    """Run the HIP AllReduce on host inputs (or on `dev_inputs`, already on the
+    device, when given); returns the device outputs."""
+    R = len(dev_inputs) if dev_inputs is not None else len(xs)
     channel(R)
     ins = dev_inputs if dev_inputs is not None else [to_device(x, dtype) for x in xs]
     if in_place:
@@ -108,6 +110,20 @@ def assert_matches_oracle_on_device(outs, want: np.ndarray, dtype: str, what: st
     ok = same | (gn & wn)
     bad = torch.nonzero(~ok).flatten()[:8].cpu().tolist()
     assert not bad, f"{what}: elements differ, first at {bad}"
+
+
+def oracle_full(xs, dtype: str) -> np.ndarray:
+    """The oracle's whole result for buffers too large for the NumPy oracle to
+    finish quickly: the plain-C oracle (checked bit for bit against the NumPy
+    oracle in tests/test_oracle_c.py), on at most 16 host threads, writing one
+    output array."""
+    import os
+
+    from oracle import cpu as C
+
+    out = np.empty(len(xs[0]), dtype=xs[0].dtype)
+    C.allreduce(xs, dtype, nthreads=min(16, os.cpu_count() or 1), outputs=[out] * len(xs))
+    return out
 
 
 def sample_indices(n: int, k: int = 1 << 16, seed: int = 0) -> np.ndarray:

@@ -63,7 +63,7 @@ def test_bad_nranks(R):
 def test_bad_dtype_and_algo():
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 3, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, -1, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
-    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 5, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 6, 0) == M.ERR_INVALID_ARGUMENT
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, -1, 0) == M.ERR_INVALID_ARGUMENT
 
 
@@ -113,11 +113,14 @@ def test_size_overflow():
 
 
 def test_selector():
-    # one-shot up to a limit that falls with R, fused two-shot up to a limit that falls with R, two-shot above
+    # one-shot up to a limit that falls with R, fused two-shot (with its
+    # completion barrier) up to a limit, two-shot above; bytes per rank buffer
     KiB, MiB = 1024, 1024 * 1024
-    fused_limit = {3: 96 * MiB, 4: 32 * MiB, 6: 16 * MiB, 7: 8 * MiB, 8: 8 * MiB, 9: 4 * MiB, 16: 4 * MiB}
-    for R, limit in ((3, 512 * KiB), (4, 512 * KiB), (5, 128 * KiB), (6, 128 * KiB), (7, 128 * KiB), (8, 128 * KiB),
-                     (9, 64 * KiB), (16, 64 * KiB)):
+    one_limit = {2: 8 * MiB, 3: 2 * MiB, 4: MiB, 5: MiB, 6: 512 * KiB, 7: 512 * KiB, 8: 256 * KiB, 9: 256 * KiB,
+                 11: 256 * KiB, 12: 128 * KiB, 16: 128 * KiB}
+    fused_limit = {4: 16 * MiB, 5: 8 * MiB, 6: MiB, 7: MiB, 8: 2 * MiB, 9: MiB, 11: MiB, 12: MiB, 15: MiB,
+                   16: 256 * KiB}
+    for R, limit in one_limit.items():
         assert M.select_algo(1, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2, M.BFLOAT16, R) == M.ALGO_ONE_SHOT
         assert M.select_algo(limit // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
@@ -128,16 +131,14 @@ def test_selector():
             assert M.select_algo(f // 2, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
             assert M.select_algo(f // 2 + 1, M.BFLOAT16, R) == M.ALGO_TWO_SHOT
             assert M.select_algo(f // 4 + 1, M.FLOAT32, R) == M.ALGO_TWO_SHOT
-        else:  # R = 5: fused at every size
+        else:  # R = 2, 3: fused at every size above the one-shot band
             assert M.select_algo(2 ** 40, M.BFLOAT16, R) == M.ALGO_TWO_SHOT_FUSED
     assert M.select_algo(1, M.BFLOAT16, 1) == M.ALGO_ONE_SHOT
     assert M.select_algo(2 ** 40, M.BFLOAT16, 1) == M.ALGO_ONE_SHOT  # one buffer: a copy at every size
-    assert M.select_algo(32 * MiB, M.BFLOAT16, 2) == M.ALGO_ONE_SHOT  # 64 MiB per rank
-    assert M.select_algo(32 * MiB + 1, M.BFLOAT16, 2) == M.ALGO_TWO_SHOT_FUSED
-    assert M.select_algo(2 ** 40, M.BFLOAT16, 2) == M.ALGO_TWO_SHOT_FUSED
     assert M.select_algo(4096, M.FLOAT32, 4) == M.ALGO_ONE_SHOT  # the 16 KiB integer workload
     assert M.select_algo(32 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT_FUSED  # 512 KiB decode shape
     assert M.select_algo(8192 * 8192, M.BFLOAT16, 8) == M.ALGO_TWO_SHOT  # 128 MiB prefill shape
+    assert M.select_algo(2 ** 24 - 1, M.BFLOAT16, 16) == M.ALGO_TWO_SHOT  # ragged R = 16 workload
     with pytest.raises(M.MsclError):
         M.select_algo(10, 7, 8)
     with pytest.raises(M.MsclError):

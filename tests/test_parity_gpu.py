@@ -114,33 +114,29 @@ def test_ragged_outliers_full(algo):
 
 
 def test_fp16_sweep():
-    """1 KiB .. 256 MiB per buffer, R = 8, every algorithm.  Up to 16 MiB the
-    whole result is compared with the oracle; above, 64 Ki sampled elements
-    (plus both ends) are, and the algorithms must agree bit for bit on every
-    element."""
+    """1 KiB .. 256 MiB per buffer, R = 8, every algorithm, every element
+    compared with the oracle: the NumPy oracle on the host up to 16 MiB, the
+    plain-C oracle with the comparison on the device above (32 .. 256 MiB,
+    where the two-shot runs held in LDS or in 2 .. 16 held slices).  The
+    algorithms must also agree with each other bit for bit."""
     for k in range(10, 29):
         w = W.sweep_fp16(k)
         xs = W.generate_all(w)
         dev_in = [G.to_device(x, "fp16") for x in xs]
+        want = O.allreduce(xs, "fp16") if k <= 24 else G.oracle_full(xs, "fp16")
+        del xs
         res = {}
-        for algo in G.EXPLICIT:
-            G.note(f"{w.name} {algo}")
-            res[algo] = G.run(xs, "fp16", algo, dev_inputs=dev_in)
-        if k <= 24:
-            want = O.allreduce(xs, "fp16")
-            for algo, outs in res.items():
-                G.assert_matches_oracle(outs, want, "fp16", f"{w.name} {algo}")
-        else:
-            idx = G.sample_indices(w.count, seed=k)
-            want = O.allreduce_elements(xs, "fp16", idx)
-            for algo, outs in res.items():
-                G.assert_outputs_equal_each_other(outs)
-                got = G.to_host_bits(outs[0], "fp16")[idx]
-                assert np.array_equal(got, want.view(np.uint16)), f"{w.name} {algo}: sampled mismatch"
-            for r in range(8):
-                for algo in ("two_shot", "two_shot_fused", "two_shot_port"):
-                    assert torch.equal(res["one_shot"][r].view(torch.uint8), res[algo][r].view(torch.uint8))
-        del dev_in, res
+        for algo in G.EXPLICIT + ("auto",):
+            plan = M.channel_plan(G.channel(8), w.count, M.FLOAT16, G.ALGOS[algo])
+            G.note(f"{w.name} {algo} (slices {plan.slices}, held tiles {plan.held_tiles})")
+            res[algo] = G.run(None, "fp16", algo, dev_inputs=dev_in)
+            if k <= 24:
+                G.assert_matches_oracle(res[algo], want, "fp16", f"{w.name} {algo}")
+            else:
+                G.assert_matches_oracle_on_device(res[algo], want, "fp16", f"{w.name} {algo}")
+        for algo in res:
+            assert torch.equal(res["one_shot"][0].view(torch.uint8), res[algo][0].view(torch.uint8))
+        del dev_in, res, want
         torch.cuda.empty_cache()
 
 
@@ -214,23 +210,20 @@ def test_two_channel_sets_on_two_streams_concurrently():
 
 
 def test_fp32_large_every_algorithm():
-    """fp32 at 32 MiB per rank, R = 8: 64 Ki sampled elements (and both ends)
-    against the oracle, and every algorithm bit-identical to the others on
-    every element."""
+    """fp32 at 32 MiB per rank (plus a 3-element tail), R = 8: every element of
+    every algorithm's result against the plain-C oracle, compared on the
+    device, and every algorithm bit-identical to the others."""
     w = W.custom(8, "fp32", (32 << 20) // 4 + 3, "normal", seed_index=33)
     xs = W.generate_all(w)
-    idx = G.sample_indices(w.count, seed=33)
-    want = O.allreduce_elements(xs, "fp32", idx)
+    want = G.oracle_full(xs, "fp32")
     dev_in = [G.to_device(x, "fp32") for x in xs]
     res = {}
-    for algo in G.EXPLICIT:
+    for algo in G.EXPLICIT + ("auto",):
         G.note(f"fp32 R=8 32 MiB {algo}")
-        res[algo] = G.run(xs, "fp32", algo, dev_inputs=dev_in)
-        G.assert_outputs_equal_each_other(res[algo])
-        got = G.to_host_bits(res[algo][0], "fp32")[idx]
-        assert np.array_equal(got, want.view(np.uint32)), f"fp32 {algo}: sampled mismatch"
+        res[algo] = G.run(None, "fp32", algo, dev_inputs=dev_in)
+        G.assert_matches_oracle_on_device(res[algo], want, "fp32", f"fp32 32 MiB {algo}")
     for r in range(8):
-        for algo in ("two_shot", "two_shot_fused", "two_shot_port"):
+        for algo in res:
             assert torch.equal(res["one_shot"][r].view(torch.uint8), res[algo][r].view(torch.uint8))
 
 
@@ -272,7 +265,8 @@ def test_graph_capture_and_replay():
     want = O.allreduce(xs, "bf16")
     ins = [G.to_device(x, "bf16") for x in xs]
     G.channel(R)
-    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT):
+    for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT,
+                 M.ALGO_TWO_SHOT_FUSED_NOBARRIER):
         outs = [G.poison_like(t) for t in ins]
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -344,14 +338,16 @@ def test_graph_capture_of_held_and_sliced_two_shots():
 
 
 @pytest.mark.parametrize("algo,in_place", [(M.ALGO_TWO_SHOT, False), (M.ALGO_ONE_SHOT, True),
-                                           (M.ALGO_TWO_SHOT_PORT, False)])
+                                           (M.ALGO_TWO_SHOT_PORT, False), (M.ALGO_TWO_SHOT_FUSED, False),
+                                           (M.ALGO_TWO_SHOT_FUSED, True)])
 def test_timeout_is_reported_not_hung(algo, in_place):
     """Force a missing signal from the host (rank 1 skips signal(), or with
     the port channel posts no puts) with a 2 ms bound on every wait(): the
     kernel must exit, the status must read TIMEOUT, further calls must refuse
     until reset, and a reset must bring the channel back.  The two-shot's
-    arrival-only barrier, the in-place one-shot's after-reads barrier, and
-    the port channel's wait for the proxy."""
+    arrival-only barrier, the in-place one-shot's after-reads barrier, the
+    port channel's wait for the proxy, and the fused two-shot's completion
+    barrier."""
     R, n = 4, 100_000
     xs = P.rand_inputs(R, n, "fp32", seed=31)
     want = O.allreduce(xs, "fp32")
@@ -372,7 +368,8 @@ def test_timeout_is_reported_not_hung(algo, in_place):
         M.channel_set_fault_controls(h, 0, -1)
         M.channel_reset(h)
     assert M.channel_check(h) == M.SUCCESS
-    names = {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_ONE_SHOT: "one_shot", M.ALGO_TWO_SHOT_PORT: "two_shot_port"}
+    names = {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_ONE_SHOT: "one_shot", M.ALGO_TWO_SHOT_PORT: "two_shot_port",
+             M.ALGO_TWO_SHOT_FUSED: "two_shot_fused"}
     outs = G.run(xs, "fp32", names[algo], in_place=in_place)
     G.assert_matches_oracle(outs, want, "fp32", "after reset")
 
@@ -485,6 +482,51 @@ def test_two_shot_in_held_slices(R, n):
         G.assert_matches_oracle(outs, want, dtype, f"two_shot sliced R={R} n={n} in_place={in_place}")
 
 
+@pytest.mark.parametrize("extra_tiles,tail", [(0, 0), (1, 0), (0, 5)],
+                         ids=["40_tiles_full_lds", "41_tiles_first_sliced", "40_tiles_plus_tail_sliced"])
+def test_held_planner_edges(extra_tiles, tail):
+    """The held two-shot at the edge of LDS: R = 8 bf16 with exactly 40 full
+    tiles per workgroup (all 160 KiB of a compute unit's LDS, one launch), one
+    tile more (the first size that runs in slices), and 40 tiles plus a ragged
+    tail (chunks round up to whole pages, so it slices too).  Out of place and
+    in place, every element against the oracle."""
+    R, dtype = 8, "bf16"
+    h = G.channel(R)
+    b = M.channel_plan(h, 8 << 20, M.BFLOAT16, M.ALGO_TWO_SHOT).workgroups_per_rank
+    tile_elems = 256 * 8  # 256 lanes x one 16-byte vector of bf16
+    n = R * (40 + extra_tiles) * b * tile_elems + tail
+    xs = W.generate_all(W.custom(R, dtype, n, "normal", seed_index=40 + extra_tiles + tail))
+    want = G.oracle_full(xs, dtype)
+    for in_place in (False, True):
+        plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_TWO_SHOT, in_place=in_place)
+        if extra_tiles == 0 and tail == 0:
+            assert plan.slices == 1 and plan.held_tiles == 40
+        else:
+            assert plan.slices >= 2 and 16 <= plan.held_tiles <= 40
+        G.note(f"held edge R={R} n={n} in_place={in_place} slices={plan.slices} held={plan.held_tiles}")
+        outs = G.run(xs, dtype, "two_shot", in_place=in_place)
+        G.assert_matches_oracle_on_device(outs, want, dtype, f"held edge n={n} in_place={in_place}")
+        del outs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("R,n", [(8, 12_000_007), (8, 24_000_017), (16, 9_000_011)],
+                         ids=["r8_held", "r8_sliced", "r16_held"])
+def test_two_shot_held_fp16(R, n):
+    """The held two-shot (one launch or slices) on fp16, with a ragged tail,
+    out of place and in place, against the oracle."""
+    dtype = "fp16"
+    h = G.channel(R)
+    xs = P.rand_inputs(R, n, dtype, seed=n % 967)
+    want = G.oracle_full(xs, dtype)
+    for in_place in (False, True):
+        plan = M.channel_plan(h, n, M.FLOAT16, M.ALGO_TWO_SHOT, in_place=in_place)
+        assert 16 <= plan.held_tiles <= 40
+        G.note(f"two_shot held fp16 R={R} n={n} in_place={in_place} slices={plan.slices} held={plan.held_tiles}")
+        outs = G.run(xs, dtype, "two_shot", in_place=in_place)
+        G.assert_matches_oracle(outs, want, dtype, f"held fp16 R={R} n={n} in_place={in_place}")
+
+
 def test_plan_geometry():
     # no LDS hold below R = 6
     r5 = M.channel_plan(G.channel(5), 30_000_007, M.BFLOAT16, M.ALGO_TWO_SHOT)
@@ -497,13 +539,15 @@ def test_plan_geometry():
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 0
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
-    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.uses_barrier == 0  # in place skips the one-shot band
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.uses_barrier == 1  # in place skips the one-shot band
     q = M.channel_plan(h, 8192 * 8192, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
     assert q.algo == M.ALGO_TWO_SHOT and q.uses_barrier == 1
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_ONE_SHOT, in_place=True)
     assert q.algo == M.ALGO_ONE_SHOT and q.uses_barrier == 1
     q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED)
-    assert q.uses_barrier == 0
+    assert q.uses_barrier == 1  # the completion barrier
+    q = M.channel_plan(h, 8192, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED_NOBARRIER)
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED_NOBARRIER and q.uses_barrier == 0
     # the fused two-shot halves its workgroups when 256-lane tiles cannot fill them
     q = M.channel_plan(h, W.decode_bf16().count, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
     assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.threads_per_workgroup == 128 and q.workgroups_per_rank == 32
@@ -521,9 +565,13 @@ def test_plan_geometry():
     assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 32
     mib8 = (8 << 20) // 2
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_AUTO)
-    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.cached_puts == 1
+    assert q.algo == M.ALGO_TWO_SHOT and q.cached_puts == 1
     q = M.channel_plan(h, mib8 + 8, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_TWO_SHOT and q.cached_puts == 0
+    q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
+    assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.cached_puts == 1 and q.uses_barrier == 1
+    q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED_NOBARRIER)
+    assert q.cached_puts == 1 and q.uses_barrier == 0
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_TWO_SHOT)
     assert q.cached_puts == 1 and q.held_tiles == 0  # 8 tiles per workgroup: too few to hold
     for algo in (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_PORT):  # not a put policy of theirs
