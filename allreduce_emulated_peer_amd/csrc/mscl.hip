@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -29,8 +30,18 @@ using namespace mscl;
 
 thread_local std::string g_last_error;
 
+int log_level();
+
+// MSCL_LOG (environment, read once): 0 (default) silent; 1 every failure a
+// call returns; 2 also each call's plan and each channel set's geometry;
+// 3 also every kernel launch.  Lines go to stderr, prefixed "[mscl]".
+void log_line(int level, const std::string& msg) {
+  if (log_level() >= level) fprintf(stderr, "[mscl] %s\n", msg.c_str());
+}
+
 mscl_status_t fail(mscl_status_t s, const std::string& msg) {
   g_last_error = msg;
+  log_line(1, "error " + std::to_string(s) + ": " + msg);
   return s;
 }
 
@@ -64,6 +75,7 @@ struct Config {
   uint64_t wait_timeout_us;  // default bound of one device-side wait
   size_t cached_puts_max_footprint;  // bound on 2*R*S for device-scope puts (SIZE_MAX = built-in)
   bool two_shot_hold;                // the two-shot may keep reduced tiles in LDS (mscl_twoshot_held)
+  int log_level;                     // MSCL_LOG: 0..3
 };
 
 const Config& config() {
@@ -75,10 +87,25 @@ const Config& config() {
     c.wg_per_rank = env_size("MSCL_WG_PER_RANK", 0);
     c.cached_puts_max_footprint = env_size("MSCL_CACHED_PUTS_MAX_BYTES", SIZE_MAX);
     c.two_shot_hold = env_size("MSCL_TWO_SHOT_HOLD", 1) != 0;
+    c.log_level = static_cast<int>(std::min<size_t>(env_size("MSCL_LOG", 0), 3));
     // clamped to a day, so the microsecond count (and its tick count) cannot wrap
     c.wait_timeout_us = std::min<size_t>(env_size("MSCL_WAIT_TIMEOUT_MS", 2000), size_t(86400000)) * 1000;
   });
   return c;
+}
+
+int log_level() { return config().log_level; }
+
+const char* algo_name(int algo) {
+  switch (algo) {
+    case MSCL_ALGO_AUTO: return "auto";
+    case MSCL_ALGO_ONE_SHOT: return "one_shot";
+    case MSCL_ALGO_TWO_SHOT: return "two_shot";
+    case MSCL_ALGO_TWO_SHOT_FUSED: return "two_shot_fused";
+    case MSCL_ALGO_TWO_SHOT_PORT: return "two_shot_port";
+    case MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER: return "two_shot_fused_nobarrier";
+  }
+  return "?";
 }
 
 }  // namespace
@@ -409,6 +436,9 @@ mscl_status_t launch(int kind, int dtype, int nranks, KernelArgs& a, void* strea
   KernelFn fn = kernel_lookup(kind, dtype, nranks);
   if (!fn) return fail(MSCL_ERR_INVALID_ARGUMENT, "no kernel for this dtype and rank count");
   const dim3 grid(static_cast<unsigned>(nranks) * a.nblk);
+  if (log_level() >= 3)
+    log_line(3, "launch kind " + std::to_string(kind) + " grid " + std::to_string(grid.x) + " x " +
+                    std::to_string(threads_for_kind(kind)) + " count " + std::to_string(a.count));
   void* kargs[] = {&a};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, dim3(threads_for_kind(kind)), kargs, 0,
                                  static_cast<hipStream_t>(stream));
@@ -542,6 +572,14 @@ mscl_status_t launch_allreduce(const mscl_channel_s* ch, const KernelArgs& proto
                                bool in_place, void* stream) {
   mscl_plan_t plan;
   make_plan(ch, count, dtype, resolved, in_place, &plan);
+  if (log_level() >= 2)
+    log_line(2, "allreduce R=" + std::to_string(nranks) + " count=" + std::to_string(count) + " dtype=" +
+                    std::to_string(dtype) + (in_place ? " in place" : "") + ": " + algo_name(plan.algo) + ", " +
+                    std::to_string(plan.workgroups_per_rank) + " workgroups/rank x " +
+                    std::to_string(plan.threads_per_workgroup) + " threads, barrier " +
+                    std::to_string(plan.uses_barrier) + ", chunk " + std::to_string(plan.chunk_elems) +
+                    ", cached_puts " + std::to_string(plan.cached_puts) + ", held_tiles " +
+                    std::to_string(plan.held_tiles) + ", slices " + std::to_string(plan.slices));
   const size_t e = elem_bytes(dtype);
   const size_t step = plan.slices > 1 ? plan.slice_elems : count;
   for (size_t lo = 0; lo < count; lo += step) {
@@ -592,6 +630,9 @@ mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, msc
     return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (count > SIZE_MAX / elem_bytes(dtype)) return fail(MSCL_ERR_INVALID_ARGUMENT, "size overflows");
   *out = resolve_algo(count, dtype, nranks, MSCL_ALGO_AUTO, /*in_place=*/false);
+  if (log_level() >= 2)
+    log_line(2, "select R=" + std::to_string(nranks) + " count=" + std::to_string(count) + " dtype=" +
+                    std::to_string(dtype) + ": " + algo_name(*out));
   return MSCL_SUCCESS;
 }
 
@@ -664,6 +705,9 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
   (void)hipSetDevice(prev);
   g_registry[key] = ch;
   *out = ch;
+  log_line(2, "channel set R=" + std::to_string(nranks) + " device " + std::to_string(device) + ": " +
+                  std::to_string(ch->cus) + " compute units, " + std::to_string(ch->slots) + " slots, " +
+                  std::to_string(ch->held_slots) + " held slots");
   return MSCL_SUCCESS;
 }
 

@@ -22,10 +22,19 @@
  * this is the reading taken, and it makes one-shot and two-shot results
  * bit-identical to each other.
  *
- * Threading.  Calls on one channel set (one device, one R) share its
- * semaphores, so they must be ordered on one stream (or otherwise
- * serialised); different channel sets are independent.  The registry itself
- * is thread-safe.
+ * Threading and concurrency.  Calls on one channel set (one device, one R)
+ * share its semaphores, so they must be ordered on one stream (or otherwise
+ * serialised).  Every kernel that runs a barrier (mscl_plan_t.uses_barrier)
+ * needs all of its workgroups resident at once, and each launch is sized to
+ * fit an otherwise idle device.  Kernels without a barrier running at the
+ * same time on other streams only delay such a launch.  Two barrier-running
+ * calls on different channel sets may overlap on concurrent streams only if
+ * their grids fit the device together; the held two-shot
+ * (mscl_plan_t.held_tiles > 0) takes all of a compute unit's LDS, so it must
+ * not overlap any other barrier-running call (order such calls with events,
+ * or run them on one stream).  A call that breaks this does not hang: its
+ * bounded waits expire, TIMEOUT is recorded, and its outputs are wrong.  The
+ * registry itself is thread-safe.
  *
  * Errors.  Every entry point returns a status code and never aborts.  The
  * text of the last failure on the calling thread is available from
@@ -110,13 +119,25 @@ typedef struct {
   size_t slice_elems;        /* elements per slice (count when slices == 1) */
 } mscl_plan_t;
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/*
+ * Library version as MAJOR*10000 + MINOR*100 + PATCH.  The pages are silent
+ * on versioning; this is bookkeeping of this library.  Never fails.
+ */
 int mscl_version(void);
 
-/* Static text for a status code ("unknown status" for anything else). */
+/*
+ * Static text for a status code ("unknown status" for anything else).  The
+ * pages are silent on error reporting; the codes are this library's (every
+ * entry point returns one instead of aborting).  The string is owned by the
+ * library and lives as long as the process.  Never fails.
+ */
 const char* mscl_status_string(mscl_status_t status);
 
-/* Text describing the most recent failure on the calling thread ("" if none). */
+/*
+ * Text describing the most recent failure on the calling thread ("" if
+ * none).  The pages are silent; this library's diagnostics.  The string is
+ * owned by the library and valid until the thread's next failing call.
+ */
 const char* mscl_last_error_string(void);
 
 /*
@@ -142,8 +163,13 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out);
 /*
  * Drop one reference; the state is freed when the count reaches zero (the
  * port channel's proxy thread, if one was started, is stopped and joined
- * first).  The caller must have synchronised every stream that used the set;
- * graphs captured with calls on it must not be replayed afterwards.
+ * first).  The pages describe channels built by host code at start-up
+ * (MSCCL++ README, Key Concepts, "On-GPU Communication Interfaces:
+ * Channels") and are silent on their teardown; this is the counterpart of
+ * mscl_channel_create.  The caller must have synchronised every stream that
+ * used the set; graphs captured with calls on it must not be replayed
+ * afterwards.
+ *   channel : a handle from mscl_channel_create (not yet fully released).
  * Errors: INVALID_ARGUMENT (null or unknown handle), HIP.
  */
 mscl_status_t mscl_channel_destroy(mscl_channel_t channel);
@@ -152,16 +178,21 @@ mscl_status_t mscl_channel_destroy(mscl_channel_t channel);
  * Report a failure recorded by an earlier call on this set: a wait() that
  * ran out of time (TIMEOUT), or a port-channel request the proxy refused
  * (INVALID_ARGUMENT: a range outside the device allocations) or could not
- * issue (HIP).  Reads the host-mapped status word; it does not synchronise,
- * so synchronise the stream first for a complete answer.  Returns SUCCESS or
- * the recorded code.
+ * issue (HIP).  The pages' wait() blocks until the peer signals (MSCCL++
+ * README, Key Concepts, "On-GPU Communication Interfaces: Channels") and are
+ * silent on a peer that never does; bounding the wait and recording the
+ * failure here is this library's reading.  Reads the host-mapped status
+ * word; it does not synchronise, so synchronise the stream first for a
+ * complete answer.  Returns SUCCESS or the recorded code (INVALID_ARGUMENT
+ * also for a null or unknown handle).
  */
 mscl_status_t mscl_channel_check(mscl_channel_t channel);
 
 /*
  * Zero the semaphores, the consumed-signal counters and the status word
  * (synchronous; the device must be idle on this set).  Needed after a
- * TIMEOUT, whose missing signals leave the counters out of step.  A port
+ * TIMEOUT, whose missing signals leave the counters out of step.  The pages
+ * are silent on recovery from a lost signal; this is the library's.  A port
  * channel keeps its allocations (graphs captured earlier still point at
  * them): its proxy is stopped, its ring and counters zeroed, and the proxy
  * started again.
@@ -170,7 +201,13 @@ mscl_status_t mscl_channel_check(mscl_channel_t channel);
 mscl_status_t mscl_channel_reset(mscl_channel_t channel);
 
 /*
- * AllReduce (sum) over R emulated ranks.
+ * AllReduce (sum) over R emulated ranks: the collective MSCCL++ accelerates
+ * for tensor-parallel LLM serving (MSCCL++ project summary, "Highlighted
+ * Details"), built on MemoryChannel-style device methods (MSCCL++ README,
+ * Key Concepts, "On-GPU Communication Interfaces: Channels": put, signal,
+ * wait; "PortChannel and MemoryChannel": many GPU threads loading and
+ * storing the peer's memory).  The name and parameter list are fixed by the
+ * target specification, which the pages do not give.
  *   inputs  : host array of nranks device pointers; inputs[r] is rank r's
  *             buffer of `count` elements.  Read only.  Inputs may alias each
  *             other.
@@ -198,9 +235,10 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * element range, launched back to back on `stream` (mscl_channel_plan
  * reports the slices); the result is the same, as the sum is elementwise.
  * That held two-shot uses all of each compute unit's LDS, one workgroup per
- * compute unit; LDS-heavy kernels running at the same time on other streams
- * can delay its workgroups past the wait bound (TIMEOUT is then recorded);
- * MSCL_TWO_SHOT_HOLD=0 (environment, read once) avoids it.
+ * compute unit: kernels on other streams that hold LDS delay its workgroups
+ * until they finish, and another barrier-running call must not overlap it
+ * (see Threading above); MSCL_TWO_SHOT_HOLD=0 (environment, read once)
+ * avoids the kernel.
  * Cache policy of the two-shot kernels' puts: when the call's footprint
  * (R inputs + R outputs, 2*R*count*element size) is at most 128 MiB they
  * are device-scope temporal stores, which leave the outputs in the
@@ -250,7 +288,9 @@ mscl_status_t mscl_reduce_scatter(const void* const inputs[], void* const output
 
 /*
  * AllGather over R emulated ranks — the two-shot's second half as a standard
- * collective.
+ * collective (the pages' library offers the usual collective interface:
+ * MSCCL++ ASPLOS'26 abstract; the data moves by MemoryChannel puts: MSCCL++
+ * README, Key Concepts, "On-GPU Communication Interfaces: Channels").
  *   inputs    : host array of nranks device pointers; inputs[r] holds
  *               sendcount elements.  Read only.
  *   outputs   : host array of nranks device pointers; outputs[p] receives
@@ -271,17 +311,21 @@ mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], 
 
 /*
  * The algorithm MSCL_ALGO_AUTO resolves to for an out-of-place call of this
- * size (bytes = count * element size), from crossovers measured on MI355X:
- *   one-shot        bytes <= 64 MiB (R <= 2), 512 KiB (R <= 4),
- *                   128 KiB (R <= 8), 64 KiB (R <= 16);
- *   fused two-shot  bytes <= 4 MiB (R >= 9), 8 MiB (R = 7 and 8),
- *                   16 MiB (R = 6), 32 MiB (R = 4), 96 MiB (R = 3), every
- *                   size (R = 2 and 5);
+ * size (bytes = count * element size).  The target specification asks for
+ * one-shot and two-shot variants switched by message size; the pages are
+ * silent on the switch point, so the bands are crossovers measured on
+ * MI355X (every band's algorithm carries the method's synchronisation):
+ *   one-shot        bytes <= 8 MiB (R <= 2), 2 MiB (R = 3), 1 MiB (R = 4
+ *                   and 5), 512 KiB (R = 6 and 7), 256 KiB (R = 8..11),
+ *                   128 KiB (R = 12..16);
+ *   fused two-shot  (with its completion barrier) bytes <= 256 KiB
+ *                   (R = 16), 1 MiB (R = 6, 7 and 9..15), 2 MiB (R = 8),
+ *                   8 MiB (R = 5), 16 MiB (R = 4), every size (R = 2, 3);
  *   two-shot        above.
  * In-place calls (any outputs[r] == inputs[r]) skip the one-shot band: in
- * place the one-shot needs a barrier between loads and stores, the fused
- * two-shot none; in place the fused two-shot also takes every size at
- * R <= 6 (mscl_channel_plan reports the in-place choice).  Pure host
+ * place the one-shot needs a barrier between loads and stores; in place the
+ * fused band also reaches 8 MiB at R = 8 and every size at R = 5
+ * (mscl_channel_plan reports the in-place choice).  Pure host
  * computation.  MSCL_ONESHOT_MAX_BYTES (environment, read once) replaces the
  * one-shot limit for every R.
  * Errors: INVALID_ARGUMENT.
@@ -290,14 +334,19 @@ mscl_status_t mscl_select_algo(size_t count, mscl_dtype_t dtype, int nranks, msc
 
 /*
  * The launch geometry mscl_allreduce would use on this channel set for this
- * size and algorithm (in_place: 1 if any outputs[r] == inputs[r]).  Pure host
- * computation.  Errors: INVALID_ARGUMENT.
+ * size and algorithm (in_place: 1 if any outputs[r] == inputs[r]).  The pages
+ * are silent on launch geometry; this exposes the library's own planner to
+ * tests and tools.  Pure host computation; writes *plan.
+ * Errors: INVALID_ARGUMENT (null plan, unknown handle, dtype or algo, or a
+ * size that overflows).
  */
 mscl_status_t mscl_channel_plan(mscl_channel_t channel, size_t count, mscl_dtype_t dtype,
                                 mscl_algo_t algo, int in_place, mscl_plan_t* plan);
 
 /*
- * Failure-handling controls for tests (never needed in normal use).
+ * Failure-handling controls for tests (never needed in normal use).  The
+ * pages are silent on failure handling; these let tests force the bounded
+ * wait of this library's wait() (see mscl_channel_check) from the host.
  *   wait_timeout_us : bound on every device-side wait() of later calls on
  *                     this set, in microseconds, at most a day (0 restores
  *                     the default of MSCL_WAIT_TIMEOUT_MS or 2000 ms).

@@ -209,6 +209,38 @@ def test_two_channel_sets_on_two_streams_concurrently():
     assert M.channel_check(G.channel(4)) == M.SUCCESS and M.channel_check(G.channel(8)) == M.SUCCESS
 
 
+def test_held_two_shot_beside_lds_kernels_on_another_stream():
+    """The held two-shot takes all of a compute unit's LDS, one workgroup per
+    compute unit, and its barrier needs every workgroup resident.  Kernels
+    that hold LDS on another stream (torch GEMMs here) can only delay its
+    workgroups until they finish: ten calls interleaved with ten 4096^3 GEMMs
+    on a second stream must all succeed, bit-exact."""
+    R, n = 8, (32 << 20) // 2  # 32 MiB per rank: 32 held tiles per workgroup
+    h = G.channel(R)
+    plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_AUTO)
+    assert plan.algo == M.ALGO_TWO_SHOT and plan.held_tiles == 32 and plan.slices == 1
+    xs = W.generate_all(W.custom(R, "bf16", n, "normal", seed_index=55))
+    want = G.oracle_full(xs, "bf16")
+    ins = [G.to_device(x, "bf16") for x in xs]
+    outs = [G.poison_like(t) for t in ins]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    a = torch.randn(4096, 4096, device="cuda", generator=gen)
+    b = torch.randn(4096, 4096, device="cuda", generator=gen)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    G.note("held two-shot x10 beside fp32 GEMMs on a second stream")
+    prods = []
+    for _ in range(10):
+        with torch.cuda.stream(side):
+            prods.append(torch.mm(a, b))
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, M.ALGO_AUTO,
+                    main.cuda_stream)
+    torch.cuda.synchronize()
+    assert M.channel_check(h) == M.SUCCESS
+    G.assert_matches_oracle_on_device(outs, want, "bf16", "held two-shot beside GEMMs")
+
+
 def test_fp32_large_every_algorithm():
     """fp32 at 32 MiB per rank (plus a 3-element tail), R = 8: every element of
     every algorithm's result against the plain-C oracle, compared on the
