@@ -20,6 +20,14 @@
 #include "kernels.hpp"
 #include "port_proxy.hpp"
 
+// Channel state of mscl_allreduce_noalloc (see there): 64 KiB of device
+// memory in the library's code object, one copy per device the library runs
+// on, held until the process ends.  Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): it uses the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchWords = (size_t(64) << 10) / sizeof(uint32_t);
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
@@ -601,6 +609,74 @@ mscl_status_t launch_allreduce(const mscl_channel_s* ch, const KernelArgs& proto
   return MSCL_SUCCESS;
 }
 
+// ----------------------------------------------------------------------------
+// Allocation-free AllReduce (mscl_allreduce_noalloc): the channel state lives
+// in `scratch`, a device array of the library's own code object, so the call
+// allocates nothing.  Layout for R ranks and a slot stride S (per device and
+// R): inbound [R][R][S] counters, consumed [R][S] counters, then the status
+// word.  Each call clears the words it uses (a fill kernel on the stream: no
+// memset node in a captured graph) before its barrier kernels run, so a call
+// never inherits the counters of an earlier one.
+// ----------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void mscl_scratch_clear(uint32_t* p, uint32_t nwords) {
+  for (uint32_t i = threadIdx.x; i < nwords; i += kThreads) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+
+struct NoAllocDevice {
+  bool ready = false;
+  uint32_t* scratch = nullptr;  // this device's copy of `scratch` (from hipGetSymbolAddress)
+  int cus = 0;
+  uint64_t wall_clock_khz = 100000;
+  uint32_t slots[kMaxRanks + 1] = {};       // per R: slot stride (0 = not yet computed)
+  uint32_t held_slots[kMaxRanks + 1] = {};
+};
+
+std::mutex g_noalloc_mutex;
+NoAllocDevice g_noalloc[kMaxDevices];
+
+// Set-up of the current device (once) and of R on it (once): the device
+// address of `scratch`, the compute-unit count and the slot bounds.  Host
+// queries only; nothing is allocated.
+mscl_status_t noalloc_geometry(int device, int nranks, NoAllocDevice* out) {
+  if (device < 0 || device >= kMaxDevices) return fail(MSCL_ERR_INVALID_ARGUMENT, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+  NoAllocDevice& d = g_noalloc[device];
+  if (!d.ready) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(MSCL_ERR_UNSUPPORTED, std::string("this library is built for gfx950, device is ") + prop.gcnArchName);
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    d.scratch = static_cast<uint32_t*>(ptr);
+    d.cus = prop.multiProcessorCount;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+      d.wall_clock_khz = static_cast<uint64_t>(khz);
+    d.ready = true;
+  }
+  if (d.slots[nranks] == 0) {
+    uint32_t slots = 0, held = 0;
+    const hipError_t e = barrier_slots(nranks, d.cus, &slots, &held);
+    if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    // No launch has more than two workgroups per compute unit in total, so
+    // that bounds the stride too; then it must fit the array.
+    const uint32_t widest = static_cast<uint32_t>(std::max(1, 2 * d.cus / nranks));
+    const uint32_t fits = static_cast<uint32_t>((kScratchWords - 1) / (static_cast<size_t>(nranks) * nranks + nranks));
+    slots = std::min({slots, widest, fits});
+    if (slots == 0) return fail(MSCL_ERR_INVALID_ARGUMENT, "the scratch array cannot hold one barrier slot per rank");
+    d.held_slots[nranks] = std::min(held, slots);
+    d.slots[nranks] = slots;
+  }
+  *out = d;
+  return MSCL_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -801,6 +877,50 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
     a.port.fifo_mask = proxy::PortState::kEntries - 1;
   }
   return launch_allreduce(b.ch, a, inputs, outputs, count, dtype, nranks, resolved, in_place, stream);
+}
+
+mscl_status_t mscl_allreduce_noalloc(const void* const inputs[], void* const outputs[], size_t count,
+                                     mscl_dtype_t dtype, int nranks, mscl_algo_t algo, void* stream) {
+  bool in_place = false;
+  mscl_status_t st = validate_call(inputs, outputs, count, dtype, nranks, algo, &in_place);
+  if (st != MSCL_SUCCESS || count == 0) return st;
+  if (algo == MSCL_ALGO_TWO_SHOT_PORT)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "the port channel allocates its request ring: use mscl_allreduce");
+  if (nranks == 1 && in_place) return MSCL_SUCCESS;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  NoAllocDevice d;
+  if ((st = noalloc_geometry(device, nranks, &d)) != MSCL_SUCCESS) return st;
+  mscl_channel_s geom;  // geometry only: no channel state is allocated or registered
+  geom.device = device;
+  geom.nranks = nranks;
+  geom.cus = d.cus;
+  geom.slots = d.slots[nranks];
+  geom.held_slots = d.held_slots[nranks];
+
+  const mscl_algo_t resolved = resolve_algo(count, dtype, nranks, algo, in_place);
+  mscl_plan_t plan;
+  make_plan(&geom, count, dtype, resolved, in_place, &plan);
+  const uint32_t stride = geom.slots;
+  uint32_t words = static_cast<uint32_t>(static_cast<size_t>(nranks) * nranks * stride + nranks * stride + 1);
+  if (words > kScratchWords) return fail(MSCL_ERR_INVALID_ARGUMENT, "channel state exceeds the 64 KiB scratch array");
+  KernelArgs a;
+  memset(&a, 0, sizeof(a));
+  a.ch.inbound = d.scratch;
+  a.ch.consumed = d.scratch + static_cast<size_t>(nranks) * nranks * stride;
+  a.ch.status = reinterpret_cast<int*>(d.scratch + words - 1);
+  a.ch.slots = stride;
+  a.ch.drop_rank = -1;
+  a.ch.timeout_ticks = config().wait_timeout_us * d.wall_clock_khz / 1000;
+  if (plan.uses_barrier) {
+    void* kargs[] = {&d.scratch, &words};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mscl_scratch_clear), dim3(1), dim3(kThreads), kargs, 0,
+                        static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "scratch clear launch");
+  }
+  return launch_allreduce(&geom, a, inputs, outputs, count, dtype, nranks, resolved, in_place, stream);
 }
 
 mscl_status_t mscl_reduce_scatter(const void* const inputs[], void* const outputs[], size_t recvcount,

@@ -42,7 +42,7 @@ EXPORTS = (
     "mscl_version", "mscl_status_string", "mscl_last_error_string", "mscl_channel_create",
     "mscl_channel_destroy", "mscl_channel_check", "mscl_channel_reset", "mscl_allreduce",
     "mscl_select_algo", "mscl_channel_plan", "mscl_channel_set_fault_controls", "mscl_reduce_scatter",
-    "mscl_allgather", "mscl_channel_selftest",
+    "mscl_allgather", "mscl_channel_selftest", "mscl_allreduce_noalloc",
 )
 
 
@@ -91,7 +91,7 @@ def load(path: str = LIB_PATH):
     for name in ("mscl_channel_destroy", "mscl_channel_check", "mscl_channel_reset"):
         getattr(lib, name).restype = c_int
         getattr(lib, name).argtypes = [vp]
-    for name in ("mscl_allreduce",):
+    for name in ("mscl_allreduce", "mscl_allreduce_noalloc"):
         getattr(lib, name).restype = c_int
         getattr(lib, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), c_size, c_int, c_int, c_int, vp]
     for name in ("mscl_reduce_scatter", "mscl_allgather"):
@@ -142,6 +142,19 @@ def raw_allreduce(inputs, outputs, count: int, dtype: int, nranks: int, algo: in
 def allreduce(inputs, outputs, count: int, dtype: int, nranks: int, algo: int = ALGO_AUTO, stream: int = 0) -> None:
     """mscl_allreduce: `inputs` / `outputs` are sequences of device addresses."""
     _check(raw_allreduce(inputs, outputs, count, dtype, nranks, algo, stream), "mscl_allreduce")
+
+
+def raw_allreduce_noalloc(inputs, outputs, count: int, dtype: int, nranks: int, algo: int, stream: int) -> int:
+    """mscl_allreduce_noalloc with no exception: returns the status code."""
+    ins = _ptr_array(inputs) if inputs is not None else None
+    outs = _ptr_array(outputs) if outputs is not None else None
+    return load().mscl_allreduce_noalloc(ins, outs, count, dtype, nranks, algo, ctypes.c_void_p(int(stream) or None))
+
+
+def allreduce_noalloc(inputs, outputs, count: int, dtype: int, nranks: int, algo: int = ALGO_AUTO,
+                      stream: int = 0) -> None:
+    """mscl_allreduce_noalloc: mscl_allreduce with no channel set and no allocation."""
+    _check(raw_allreduce_noalloc(inputs, outputs, count, dtype, nranks, algo, stream), "mscl_allreduce_noalloc")
 
 
 def raw_reduce_scatter(inputs, outputs, recvcount: int, dtype: int, nranks: int, stream: int) -> int:

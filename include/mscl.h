@@ -263,6 +263,29 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
                              mscl_dtype_t dtype, int nranks, mscl_algo_t algo, void* stream);
 
 /*
+ * mscl_allreduce for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, algorithms and results, but no channel set is needed
+ * and nothing is allocated, neither at the first call nor later.  The
+ * channel state (semaphores, consumed-signal counters, status word) lives in
+ * a 64 KiB array in the library's device code, one per device, held until
+ * the process ends; the first call on a device looks up that array's address
+ * and the device's geometry (host queries only).  Every call clears the
+ * words its barriers use (a fill kernel on `stream`, no memset) before it
+ * launches them, so calls on one device must not overlap: two such calls
+ * running at once on different streams race on the shared array.  Launch
+ * geometry is the same as mscl_allreduce's except that the workgroups per
+ * rank are capped so that the channel state fits the array.
+ * MSCL_ALGO_TWO_SHOT_PORT is refused (INVALID_ARGUMENT): its proxy needs a
+ * request ring.  A device-side wait that runs out of time is recorded only
+ * in the array (nothing host-visible exists to report it), leaves that
+ * call's outputs wrong, and does not affect later calls.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, UNSUPPORTED, HIP.
+ */
+mscl_status_t mscl_allreduce_noalloc(const void* const inputs[], void* const outputs[], size_t count,
+                                     mscl_dtype_t dtype, int nranks, mscl_algo_t algo, void* stream);
+
+/*
  * ReduceScatter (sum) over R emulated ranks — the two-shot's first half as a
  * standard collective (the pages' library offers the usual collective
  * interface: MSCCL++ ASPLOS'26 abstract).
