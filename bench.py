@@ -265,10 +265,69 @@ def main() -> int:
         del g
         return float(np.median(ts))
 
+    def rotated_graph_us(w, ins, algo=M.ALGO_AUTO, reps=100):
+        """Device time per call over K buffer sets rotated call by call, K the
+        fewest whose footprint K * 2RS reaches 512 MiB (past the 256 MB
+        Infinity Cache and every L2), replayed from one graph ("cold")."""
+        K = max(1, -(-(512 << 20) // (2 * w.nranks * w.bytes_per_rank)))
+        sets = [(ins, [torch.empty_like(t) for t in ins])]
+        sets += [([t.clone() for t in ins], [torch.empty_like(t) for t in ins]) for _ in range(K - 1)]
+        for a_, b_ in sets:
+            caller(w, a_, b_, algo)()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = [caller(w, a_, b_, algo, on_stream=torch.cuda.current_stream()) for a_, b_ in sets]
+            for i in range(max(reps, K)):
+                cap[i % K]()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1000.0 / max(reps, K))
+        del g, sets, cap
+        return float(np.median(ts)), K
+
+    CTYPE = {"fp32": "F32", "fp16": "F16", "bf16": "BF16"}
+    ALGO_NAME = {1: "one_shot", 2: "two_shot", 3: "two_shot_fused", 4: "two_shot_port", 5: "two_shot_fused_nobarrier"}
+
+    def describe(w, algo=M.ALGO_AUTO, in_place=False):
+        """The algorithm, kernel and synchronisation a call of workload `w` runs."""
+        p = M.channel_plan(M.channel_create(w.nranks, dev), w.count, code[w.dtype], algo, in_place=in_place)
+        c, R = CTYPE[w.dtype], w.nranks
+        cached = "true" if p.cached_puts else "false"
+        if p.algo == M.ALGO_ONE_SHOT:
+            kernel = f"mscl_oneshot<{c}, {R}, {'true' if in_place else 'false'}>"
+            sync = "after-reads barrier per batch (in place)" if in_place else "none (one-shot)"
+        elif p.algo == M.ALGO_TWO_SHOT:
+            kernel = f"mscl_twoshot_held<{c}, {R}>" if p.held_tiles else f"mscl_twoshot<{c}, {R}, {cached}>"
+            sync = "signal/wait barrier between reduce-scatter and all-gather"
+        elif p.algo == M.ALGO_TWO_SHOT_FUSED:
+            kernel = f"mscl_twoshot_fused<{c}, {R}, {p.threads_per_workgroup}, {cached}, true>"
+            sync = "completion barrier after the puts"
+        elif p.algo == M.ALGO_TWO_SHOT_FUSED_NOBARRIER:
+            kernel = f"mscl_twoshot_fused<{c}, {R}, {p.threads_per_workgroup}, {cached}, false>"
+            sync = "none (labelled variant: completion is the kernel's end on the stream)"
+        else:
+            kernel = f"mscl_twoshot_port<{c}, {R}>"
+            sync = "port-channel flush (proxy completion)"
+        d = {"algo": ALGO_NAME[p.algo], "kernel": kernel, "sync": sync}
+        if p.slices > 1:
+            d["slices"] = p.slices
+        return d
+
     # ---------------------------------------------------------------- main
     w = W.prefill_bf16()
     log(f"[bench] generating {w.name}: R={w.nranks} x {w.bytes_per_rank} B")
-    ins = device_inputs(w)
+    main_xs = W.generate_all(w)  # kept on the host for the CPU baseline
+    ins = []
+    for x in main_xs:
+        ins.append(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda"))
     outs = [torch.empty_like(t) for t in ins]
     call = caller(w, ins, outs)
     plan = M.channel_plan(M.channel_create(w.nranks, dev), w.count, M.BFLOAT16, M.ALGO_AUTO)
@@ -435,7 +494,9 @@ def main() -> int:
         cold_dev = a.elapsed_time(b) * 1000.0 / (2 * K)
         del g, sets, calls, cap
         p50_te = p50_us_timing_events(caller(dw, di, do), args.latency_iters)
-        decode = {"workload": dw.name,
+        nob_us = graph_us(dw, di, do, M.ALGO_TWO_SHOT_FUSED_NOBARRIER)
+        decode = {"workload": dw.name, **describe(dw),
+                  "nobarrier_variant_graph_us_per_call": round(nob_us, 2),
                   "hot": {"p50_us": round(p50, 2), "p50_us_timing_events": round(p50_te, 2),
                           "graph_us_per_call": round(dev_us, 2),
                           "algbw_GBps_graph": round(dw.bytes_per_rank / dev_us / 1e3, 1),
@@ -457,8 +518,7 @@ def main() -> int:
         ro = [torch.empty_like(t) for t in ri]
         rplan = M.channel_plan(M.channel_create(rw.nranks, dev), rw.count, M.BFLOAT16, M.ALGO_AUTO)
         t_r = graph_us(rw, ri, ro, M.ALGO_AUTO, reps=10)
-        ragged = {"workload": rw.name, "algo": {1: "one_shot", 2: "two_shot", 3: "two_shot_fused"}[rplan.algo],
-                  "us": round(t_r, 1), "algbw_GBps": round(rw.bytes_per_rank / t_r / 1e3, 1),
+        ragged = {"workload": rw.name, **describe(rw), "us": round(t_r, 1), "algbw_GBps": round(rw.bytes_per_rank / t_r / 1e3, 1),
                   "pct_hbm_peak": round(100 * rw.algorithmic_bytes / t_r / 1e3 / HBM_PEAK_GBPS, 1)}
         log(f"[bench] {rw.name}: {t_r:.1f} us, {ragged['pct_hbm_peak']}% of HBM peak")
         del ri, ro
@@ -467,21 +527,81 @@ def main() -> int:
     size_curve = None
     if not args.main_only:
         # The metric's size range, R = 8 bf16 from 512 KiB to 128 MiB per rank,
-        # with AUTO's pick: device time per call from graph replay (hot buffers).
-        size_curve = {"note": "R=8 bf16, AUTO's pick, device time per call (graph replay, same buffers each call)"}
+        # with AUTO's pick: device time per call replayed from a graph, over the
+        # same buffers every call ("hot") and over buffer sets rotated past the
+        # Infinity Cache ("cold").  Below 32 MiB per rank the hot call's 2RS
+        # footprint fits the 256 MB Infinity Cache, so its HBM percentage
+        # measures cache bandwidth; the cold figure is the HBM one.
+        size_curve = {"note": "R=8 bf16, AUTO's pick; us per call from graph replay: hot = same buffers every call, "
+                              "cold = buffer sets rotated so that the replayed footprint reaches 512 MiB (K sets); "
+                              "pct_hbm_peak = 2RS/t over 8 TB/s; cache_resident: the hot call's 2RS fits the 256 MB "
+                              "Infinity Cache, so only its cold figure measures HBM"}
         for k in range(19, 28):
             cw = W.sweep_bf16(k)
-            ci_, co_ = device_inputs(cw), None
+            ci_ = device_inputs(cw)
             co_ = [torch.empty_like(t) for t in ci_]
-            t_c = graph_us(cw, ci_, co_, M.ALGO_AUTO, 50 if cw.bytes_per_rank <= (4 << 20) else 5)
-            pick = {1: "one_shot", 2: "two_shot", 3: "two_shot_fused"}[M.select_algo(cw.count, M.BFLOAT16, 8)]
-            size_curve[f"{cw.bytes_per_rank}B"] = {
-                "algo": pick, "us": round(t_c, 2), "algbw_GBps": round(cw.bytes_per_rank / t_c / 1e3, 1),
-                "pct_hbm_peak": round(100 * cw.algorithmic_bytes / t_c / 1e3 / HBM_PEAK_GBPS, 1)}
+            reps = 50 if cw.bytes_per_rank <= (4 << 20) else 5
+            t_h = graph_us(cw, ci_, co_, M.ALGO_AUTO, reps)
+            t_c, K = rotated_graph_us(cw, ci_, M.ALGO_AUTO, reps)
+            entry = describe(cw)
+            entry.update({
+                "hot_us": round(t_h, 2), "cold_us": round(t_c, 2), "cold_sets": K,
+                "algbw_GBps_hot": round(cw.bytes_per_rank / t_h / 1e3, 1),
+                "algbw_GBps_cold": round(cw.bytes_per_rank / t_c / 1e3, 1),
+                "pct_hbm_peak_hot": round(100 * cw.algorithmic_bytes / t_h / 1e3 / HBM_PEAK_GBPS, 1),
+                "pct_hbm_peak_cold": round(100 * cw.algorithmic_bytes / t_c / 1e3 / HBM_PEAK_GBPS, 1),
+                "cache_resident": cw.algorithmic_bytes <= (256 << 20)})
+            if entry["algo"] == "two_shot_fused":
+                entry["nobarrier_variant_hot_us"] = round(
+                    graph_us(cw, ci_, co_, M.ALGO_TWO_SHOT_FUSED_NOBARRIER, reps), 2)
+            size_curve[f"{cw.bytes_per_rank}B"] = entry
             del ci_, co_
             torch.cuda.empty_cache()
-        log(f"[bench] size curve: " + ", ".join(f"{k} {v['algbw_GBps']} GB/s" for k, v in size_curve.items()
-                                                 if k != "note"))
+        log(f"[bench] size curve (hot/cold GB/s): " + ", ".join(
+            f"{k} {v['algbw_GBps_hot']}/{v['algbw_GBps_cold']} ({v['algo']})" for k, v in size_curve.items()
+            if k != "note"))
+
+    fp16_sweep = None
+    if not args.main_only:
+        # The fp16 uniform[-1, 1] workload at R = 8, 1 KiB .. 256 MiB per rank:
+        # every algorithm's device time (graph replay, same buffers), AUTO's
+        # pick, and the crossovers.  Inputs are drawn on the device (seeded
+        # torch generator, uniform[-1, 1] in binary32 rounded to fp16): timing
+        # does not depend on the values, and host generation of 2 GiB would
+        # dominate the run.
+        fp16_sweep = {"note": "R=8 fp16 uniform[-1,1] (drawn on the device), bytes per rank 2^k; us per call from "
+                              "graph replay over the same buffers (hot: up to 16 MiB per rank the 2RS footprint "
+                              "fits the Infinity Cache); auto = AUTO's pick; crossovers: smallest size at which "
+                              "the next algorithm is faster", "points": {}}
+        gen = torch.Generator(device="cuda")
+        prev_best = None
+        cross = {}
+        for k in range(10, 29):
+            sw = W.sweep_fp16(k)
+            gen.manual_seed(20261202 + k)
+            si = [(torch.rand(sw.count, generator=gen, device="cuda") * 2 - 1).to(torch.float16)
+                  for _ in range(sw.nranks)]
+            so = [torch.empty_like(t) for t in si]
+            reps = 50 if sw.bytes_per_rank <= (4 << 20) else 5
+            t = {name: graph_us(sw, si, so, a, reps) for a, name in
+                 ((M.ALGO_ONE_SHOT, "one_shot"), (M.ALGO_TWO_SHOT, "two_shot"), (M.ALGO_TWO_SHOT_FUSED, "two_shot_fused"))}
+            d = describe(sw)
+            t_auto = t[d["algo"]]
+            best = min(t, key=t.get)
+            if prev_best is not None and best != prev_best and f"{prev_best}->{best}" not in cross:
+                cross[f"{prev_best}->{best}"] = sw.bytes_per_rank
+            prev_best = best
+            fp16_sweep["points"][str(sw.bytes_per_rank)] = {
+                "auto": d["algo"], "kernel": d["kernel"], "us": round(t_auto, 2),
+                "algbw_GBps": round(sw.bytes_per_rank / t_auto / 1e3, 1),
+                "pct_hbm_peak": round(100 * sw.algorithmic_bytes / t_auto / 1e3 / HBM_PEAK_GBPS, 1),
+                "one_shot_us": round(t["one_shot"], 2), "two_shot_us": round(t["two_shot"], 2),
+                "fused_us": round(t["two_shot_fused"], 2)}
+            del si, so
+            torch.cuda.empty_cache()
+        fp16_sweep["crossovers_bytes_per_rank"] = cross
+        fp16_sweep["p50_16KiB_graph_us"] = fp16_sweep["points"][str(16 << 10)]["us"]
+        log(f"[bench] fp16 sweep crossovers: {cross}")
 
     pipeline = None
     if not args.main_only:
@@ -689,21 +809,21 @@ def main() -> int:
         from oracle import cpu as C
 
         cores = min(os.cpu_count() or 1, 16)
-        n_sample = 1 << 24  # first 16 Mi elements (32 MiB) of each of the 8 rank buffers
-        xs = [W.generate(w, r)[:n_sample].copy() for r in range(w.nranks)]
-        outs_h = [np.empty(n_sample, dtype=np.uint16) for _ in range(w.nranks)]
-        C.allreduce(xs, "bf16", nthreads=cores, outputs=outs_h)  # warm
+        outs_h = [np.empty(w.count, dtype=np.uint16) for _ in range(w.nranks)]
+        C.allreduce(main_xs, "bf16", nthreads=cores, outputs=outs_h)  # warm (first touch of the outputs)
         reps, t_total = 0, 0.0
-        while t_total < 10.0 and reps < 50:
+        while t_total < 15.0 and reps < 60:
             t1 = time.perf_counter()
-            C.allreduce(xs, "bf16", nthreads=cores, outputs=outs_h)
+            C.allreduce(main_xs, "bf16", nthreads=cores, outputs=outs_h)
             t_total += time.perf_counter() - t1
             reps += 1
         t_per = t_total / reps
-        cpu = {"value": round(n_sample * 2 / t_per / 1e9, 3), "unit": "GB/s", "cores": cores,
+        cpu = {"value": round(w.bytes_per_rank / t_per / 1e9, 3), "unit": "GB/s", "cores": cores,
                "host_cpu_count": os.cpu_count(), "kind": "oracle",
-               "sample": f"plain-C oracle, first {n_sample} elements of each of the 8 rank buffers of {w.name}, "
-                         f"{reps} runs, {t_per * 1000:.1f} ms per run; same algbw accounting (S/t)"}
+               "sample": f"plain-C oracle on the whole {w.name} workload (8 x {w.count} bf16 elements, the same "
+                         f"inputs as the GPU run), {reps} runs, {t_per * 1000:.1f} ms per run; same algbw "
+                         f"accounting (S/t)"}
+        del outs_h
         log(f"[bench] cpu oracle: {cpu['value']} GB/s algbw on {cores} threads")
 
     line = {
@@ -721,6 +841,7 @@ def main() -> int:
         "latency": latency,
         "host_api": host,
         "algbw_512KiB_to_128MiB": size_curve,
+        "fp16_sweep_1KiB_to_256MiB": fp16_sweep,
         "decode_512KiB": decode,
         "between_producer_and_consumer": pipeline,
         "ragged_r16": ragged,
