@@ -101,6 +101,51 @@ def oracle_record() -> int:
     return 0
 
 
+def profile_legs(M, W, device_inputs, caller) -> int:
+    """Three untimed calls of every kernel the bench line reports, for
+    rocprofv3 counter passes (one kernel per dispatch, so the counters read per
+    dispatch are the kernel's own), then three plain 1 GiB device copies whose
+    known bytes calibrate the counters."""
+    import ctypes
+
+    import torch
+
+    for w in (W.prefill_bf16(), W.ragged_outliers_bf16(), W.sweep_bf16(21), W.decode_bf16()):
+        ins = device_inputs(w)
+        outs = [torch.empty_like(t) for t in ins]
+        c = caller(w, ins, outs)
+        for _ in range(3):
+            c()
+        torch.cuda.synchronize()
+        log(f"[profile-legs] {w.name}: 3 calls")
+        del ins, outs
+        torch.cuda.empty_cache()
+    w = W.prefill_bf16()
+    R, rc = w.nranks, w.count // w.nranks
+    ins = device_inputs(w)
+    blocks = [torch.empty(rc, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    gathered = [torch.empty(w.count, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    lib = M.load()
+    rs_in = (ctypes.c_void_p * R)(*[t.data_ptr() for t in ins])
+    rs_out = (ctypes.c_void_p * R)(*[t.data_ptr() for t in blocks])
+    ag_out = (ctypes.c_void_p * R)(*[t.data_ptr() for t in gathered])
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        assert lib.mscl_reduce_scatter(rs_in, rs_out, rc, M.BFLOAT16, R, s) == M.SUCCESS
+    for _ in range(3):
+        assert lib.mscl_allgather(rs_out, ag_out, rc, M.BFLOAT16, R, s) == M.SUCCESS
+    torch.cuda.synchronize()
+    log("[profile-legs] reduce_scatter and allgather of the prefill buffers: 3 calls each")
+    del ins, blocks, gathered
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[profile-legs] copy calibration: 3 plain copies of 1 GiB")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +157,10 @@ def main() -> int:
     ap.add_argument("--latency-iters", type=int, default=1000)
     ap.add_argument("--main-only", action="store_true",
                     help="time only the main workload (for profiler runs): no latency, decode or CPU legs")
+    ap.add_argument("--profile-legs", action="store_true",
+                    help="for counter runs: three untimed calls of each kernel the bench line reports (prefill, "
+                         "ragged R=16, the 2 MiB and 512 KiB R=8 calls, ReduceScatter, AllGather) and three 1 GiB "
+                         "device copies for counter calibration; prints nothing on stdout")
     ap.add_argument("--oracle-record", action="store_true",
                     help="CPU only: time the NumPy oracle (one core) and the C oracle once per workload at full size")
     args = ap.parse_args()
@@ -320,6 +369,9 @@ def main() -> int:
         if p.slices > 1:
             d["slices"] = p.slices
         return d
+
+    if args.profile_legs:
+        return profile_legs(M, W, device_inputs, caller)
 
     # ---------------------------------------------------------------- main
     w = W.prefill_bf16()
