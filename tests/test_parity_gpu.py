@@ -559,6 +559,28 @@ def test_two_shot_held_fp16(R, n):
         G.assert_matches_oracle(outs, want, dtype, f"held fp16 R={R} n={n} in_place={in_place}")
 
 
+def test_held_plans_always_hold_whole_shares():
+    """The held two-shot serves only workgroups whose whole share fits in LDS
+    (it records INVALID_ARGUMENT rather than serve part of one): over a spread
+    of ragged sizes at every rank count that holds (R >= 6), every plan (or
+    first slice) with held_tiles > 0 must give its busiest workgroup 16..40
+    full tiles, and slices must cover the call.  Host planning only."""
+    g = np.random.default_rng(2026)
+    for R in range(6, 17):
+        h = G.channel(R)
+        for n in sorted(set(int(x) for x in np.exp(g.uniform(np.log(1 << 20), np.log(300 << 20), size=60)))):
+            for dtype, V in ((M.BFLOAT16, 8), (M.FLOAT32, 4)):
+                plan = M.channel_plan(h, n, dtype, M.ALGO_TWO_SHOT)
+                assert plan.slices >= 1 and (plan.slices - 1) * plan.slice_elems < n <= plan.slices * plan.slice_elems
+                if plan.held_tiles == 0:
+                    continue
+                first = M.channel_plan(h, plan.slice_elems, dtype, M.ALGO_TWO_SHOT)
+                tiles = (first.chunk_elems // V) // 256
+                per_slot = -(-tiles // first.workgroups_per_rank)
+                assert 16 <= per_slot <= 40 and per_slot == plan.held_tiles, (R, n, dtype, per_slot, plan.held_tiles)
+                assert plan.vectors_per_thread == 1 and plan.cached_puts == 0
+
+
 def test_plan_geometry():
     # no LDS hold below R = 6
     r5 = M.channel_plan(G.channel(5), 30_000_007, M.BFLOAT16, M.ALGO_TWO_SHOT)
