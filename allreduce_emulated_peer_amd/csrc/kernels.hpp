@@ -328,36 +328,38 @@ __device__ inline Held held_range(u32x4 (*lds)[kThreads], uint64_t nfull_tiles, 
 }
 
 // Reduce-scatter: chunk `rank` of every input -> own output `mine` (or, for
-// the tiles `h` names, this lane's LDS slots).
+// the tiles `h` names, this lane's LDS slots).  The lane's vector of the
+// rank's tile t is vector lane_base + t * tstride of every buffer (tstride is
+// one tile for a contiguous chunk, R tiles for interleaved shares).
 // Software pipelined: the loads of the slot's next tile are issued before
 // the current tile is reduced and stored, so each wave keeps R*U 16-byte
 // loads in flight while it computes.
 template <class C, int R, bool kHold = false>
 __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& g, int slot, void* mine,
-                                              uint64_t lane_base, const Held h = Held{nullptr, ~0ull}) {
+                                              uint64_t lane_base, uint64_t tstride,
+                                              const Held h = Held{nullptr, ~0ull}) {
   constexpr int U = unroll_for<R>();
-  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
   const uint64_t B = a.nblk;
   if (static_cast<uint64_t>(slot) < g.nfull_tiles) {
     uint64_t t = slot;
     uint64_t j = 0;  // index of t among this slot's tiles
     u32x4 cur[U][R];
-    load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * kTile, g.v_full);
+    load_tile<R, U, true, kStreamRsLoads>(cur, a.in, lane_base + t * tstride, g.v_full);
     while (true) {
       const uint64_t tn = t + B;
       const bool more = tn < g.nfull_tiles;
       u32x4 nxt[U][R];
-      if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * kTile, g.v_full);
+      if (more) load_tile<R, U, true, kStreamRsLoads>(nxt, a.in, lane_base + tn * tstride, g.v_full);
       u32x4 y[U];
       reduce_tile<C, R, U>(y, cur);
       if constexpr (kHold && U == 1) {
         if (j >= h.first_held) {
           h.lds[j - h.first_held][threadIdx.x] = y[0];  // kept for the all-gather, read back by this lane only
         } else {
-          store_tile<U, true, Put::kCached>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather
+          store_tile<U, true, Put::kCached>(mine, y, lane_base + t * tstride, g.v_full);  // re-read by the all-gather
         }
       } else {
-        store_tile<U, true, Put::kCached>(mine, y, lane_base + t * kTile, g.v_full);  // re-read by the all-gather
+        store_tile<U, true, Put::kCached>(mine, y, lane_base + t * tstride, g.v_full);  // re-read by the all-gather
       }
       ++j;
       if (!more) break;
@@ -369,7 +371,7 @@ __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& 
   if (g.owns_partial_tile) {
     u32x4 x[U][R];
     u32x4 y[U];
-    const uint64_t base = lane_base + g.nfull_tiles * kTile;
+    const uint64_t base = lane_base + g.nfull_tiles * tstride;
     load_tile<R, U, false, kStreamRsLoads>(x, a.in, base, g.v_full);
     reduce_tile<C, R, U>(y, x);
     store_tile<U, false, Put::kCached>(mine, y, base, g.v_full);
@@ -378,7 +380,27 @@ __device__ inline void twoshot_reduce_scatter(const KernelArgs& a, const Chunk& 
     store_partial<C>(mine, g.v_full, reduce_partial<C, R>(a, g.v_full, g.ntail), g.ntail);
 }
 
-template <class C, int R, bool kCachedPuts, bool kHold>
+// A rank's share when whole tiles are dealt to the ranks in turn (tile T to
+// rank T mod R), for calls whose length is a whole number of R tiles: every
+// rank then has count / (R * tile) full tiles and nothing else.  Tile t of
+// the rank is the call's tile t * R + rank.
+template <class C, int R, int U>
+__device__ inline Chunk interleaved_share(const KernelArgs& a) {
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  Chunk g;
+  g.lo = 0;
+  g.hi = a.count;
+  g.v_lo = 0;
+  g.v_full = a.count / C::V;
+  g.ntail = 0;
+  g.nfull_tiles = g.v_full / kTile / R;
+  g.owns_partial_tile = false;
+  return g;
+}
+
+// kIlv: tiles dealt to the ranks in turn (interleaved_share) instead of one
+// contiguous chunk per rank; the host uses it only for whole-R-tile slices.
+template <class C, int R, bool kCachedPuts, bool kHold, bool kIlv = false>
 __device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads]) {
   constexpr int U = unroll_for<R>();
   constexpr Put kP = put_policy<kCachedPuts>();
@@ -386,16 +408,18 @@ __device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads])
   const int rank = blockIdx.x % R;
   const int slot = blockIdx.x / R;
   const uint64_t B = a.nblk;
-  const Chunk g = chunk_of<C, U>(a, rank, slot);
+  const Chunk g = kIlv ? interleaved_share<C, R, U>(a) : chunk_of<C, U>(a, rank, slot);
+  // vector index of this lane's vector in the rank's tile t: lane_base + t * tstride
+  const uint64_t tstride = kIlv ? kTile * R : kTile;
   const uint64_t v_full = g.v_full, nfull_tiles = g.nfull_tiles;
   const int ntail = g.ntail;
   const bool owns_partial_tile = g.owns_partial_tile;
   const RankChannels chans{a.ch, R, rank, slot};
   void* const mine = a.out[rank];
-  const uint64_t lane_base = g.v_lo + threadIdx.x;
+  const uint64_t lane_base = (kIlv ? static_cast<uint64_t>(rank) * kTile : g.v_lo) + threadIdx.x;
 
   const Held h = held_range(lds, nfull_tiles, slot, B);
-  twoshot_reduce_scatter<C, R, kHold>(a, g, slot, mine, lane_base, h);
+  twoshot_reduce_scatter<C, R, kHold>(a, g, slot, mine, lane_base, tstride, h);
   const bool tail_owner = ntail != 0 && slot == 0 && threadIdx.x == 0;
 
   // signal / wait with the same slot of every peer rank.  Arrival only: no
@@ -417,7 +441,7 @@ __device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads])
   }
   if (owns_partial_tile) {
     u32x4 y[U];
-    const uint64_t base = lane_base + nfull_tiles * kTile;
+    const uint64_t base = lane_base + nfull_tiles * tstride;
     ag_load<U, false>(y, mine, base, v_full);
     ag_store<R, U, false, kP>(a, rank, y, base, v_full);
   }
@@ -452,25 +476,25 @@ __device__ inline void twoshot_body(const KernelArgs& a, u32x4 (*lds)[kThreads])
         u32x4 y0[U], y1[U];
         y0[0] = h.lds[j - 1][threadIdx.x];
         y1[0] = h.lds[j - 2][threadIdx.x];
-        store_tile<U, true, kP>(dst, y0, lane_base + (slot + (j - 1) * B) * kTile, v_full);
-        store_tile<U, true, kP>(dst, y1, lane_base + (slot + (j - 2) * B) * kTile, v_full);
+        store_tile<U, true, kP>(dst, y0, lane_base + (slot + (j - 1) * B) * tstride, v_full);
+        store_tile<U, true, kP>(dst, y1, lane_base + (slot + (j - 2) * B) * tstride, v_full);
       }
       if (j == 1) {
         u32x4 y[U];
         y[0] = h.lds[0][threadIdx.x];
-        store_tile<U, true, kP>(dst, y, lane_base + slot * kTile, v_full);
+        store_tile<U, true, kP>(dst, y, lane_base + slot * tstride, v_full);
       }
     }
   } else {
     uint64_t t = slot + (nfull_tiles - 1 - slot) / B * B;  // this slot's last full tile
     u32x4 cur[U];
-    ag_load<U, true>(cur, mine, lane_base + t * kTile, v_full);
+    ag_load<U, true>(cur, mine, lane_base + t * tstride, v_full);
     while (true) {
       const bool more = t >= static_cast<uint64_t>(slot) + B;
       const uint64_t tn = more ? t - B : t;
       u32x4 nxt[U];
-      if (more) ag_load<U, true>(nxt, mine, lane_base + tn * kTile, v_full);
-      ag_store<R, U, true, kP>(a, rank, cur, lane_base + t * kTile, v_full);
+      if (more) ag_load<U, true>(nxt, mine, lane_base + tn * tstride, v_full);
+      ag_store<R, U, true, kP>(a, rank, cur, lane_base + t * tstride, v_full);
       if (!more) break;
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
@@ -497,11 +521,18 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
 // nothing (R = 8, 128 MiB, 40 of 128 tiles: 375 -> 377 us), and with fewer
 // tiles the all-gather's extra own-output store costs more than it saves
 // (R = 16, 8 MiB, 8 tiles: 47.7 -> 49.0 us).
-template <class C, int R>
+//
+// kIlv: the tiles of the call are dealt to the ranks in turn instead of one
+// contiguous chunk per rank, so at any moment all workgroups read and write
+// one neighbourhood of each buffer; the host uses it for the whole-R-tile
+// slices of large calls at R <= 8 (R = 8, 128 MiB in 8 slices: 347.8 ->
+// 340.9 us; 64 MiB in 4 slices: 173.5 -> 168.8 us; it loses on single held
+// launches and at R = 16).
+template <class C, int R, bool kIlv>
 __global__ __launch_bounds__(kThreads) void mscl_twoshot_held(KernelArgs a) {
   if constexpr (unroll_for<R>() == 1) {
     __shared__ u32x4 held[kHeldTiles][kThreads];
-    twoshot_body<C, R, false, true>(a, held);
+    twoshot_body<C, R, false, true, kIlv>(a, held);
   } else {
     twoshot_body<C, R, false, false>(a, nullptr);  // several vectors per lane: the host never picks this
   }
@@ -523,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_port(KernelArgs a) {
   const int slot = blockIdx.x / R;
   const Chunk g = chunk_of<C, U>(a, rank, slot);
   char* const mine = static_cast<char*>(a.out[rank]);
-  twoshot_reduce_scatter<C, R>(a, g, slot, mine, g.v_lo + threadIdx.x);
+  twoshot_reduce_scatter<C, R>(a, g, slot, mine, g.v_lo + threadIdx.x, static_cast<uint64_t>(kThreads) * U);
 
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // this thread's stores, published at system scope
   __syncthreads();
@@ -891,7 +922,8 @@ enum {
   kAlgoTwoShotFusedSync = 14,
   kAlgoTwoShotFusedHalfSync = 15,
   kAlgoTwoShotFusedCachedPutsSync = 16,
-  kAlgoTwoShotFusedHalfCachedPutsSync = 17
+  kAlgoTwoShotFusedHalfCachedPutsSync = 17,
+  kAlgoTwoShotHeldInterleaved = 18  // the held two-shot with tiles dealt to the ranks in turn
 };
 
 template <class C, int R>
@@ -909,7 +941,8 @@ constexpr KernelFn kernel_for(int kind) {
     case kAlgoTwoShotFusedHalfSync: return &mscl_twoshot_fused<C, R, kThreads / 2, false, true>;
     case kAlgoTwoShotFusedCachedPutsSync: return &mscl_twoshot_fused<C, R, kThreads, true, true>;
     case kAlgoTwoShotFusedHalfCachedPutsSync: return &mscl_twoshot_fused<C, R, kThreads / 2, true, true>;
-    case kAlgoTwoShotHeld: return &mscl_twoshot_held<C, R>;
+    case kAlgoTwoShotHeld: return &mscl_twoshot_held<C, R, false>;
+    case kAlgoTwoShotHeldInterleaved: return &mscl_twoshot_held<C, R, true>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
     case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;

@@ -65,6 +65,7 @@ class Plan(ctypes.Structure):
         ("held_tiles", ctypes.c_int),
         ("slices", ctypes.c_int),
         ("slice_elems", ctypes.c_size_t),
+        ("tile_interleave", ctypes.c_int),
     ]
 
 

@@ -354,7 +354,8 @@ def main() -> int:
             kernel = f"mscl_oneshot<{c}, {R}, {'true' if in_place else 'false'}>"
             sync = "after-reads barrier per batch (in place)" if in_place else "none (one-shot)"
         elif p.algo == M.ALGO_TWO_SHOT:
-            kernel = f"mscl_twoshot_held<{c}, {R}>" if p.held_tiles else f"mscl_twoshot<{c}, {R}, {cached}>"
+            kernel = (f"mscl_twoshot_held<{c}, {R}, {'true' if p.tile_interleave else 'false'}>" if p.held_tiles
+                      else f"mscl_twoshot<{c}, {R}, {cached}>")
             sync = "signal/wait barrier between reduce-scatter and all-gather"
         elif p.algo == M.ALGO_TWO_SHOT_FUSED:
             kernel = f"mscl_twoshot_fused<{c}, {R}, {p.threads_per_workgroup}, {cached}, true>"
@@ -388,8 +389,8 @@ def main() -> int:
         f"threads, {plan.vectors_per_thread} vectors/thread, {plan.slices} slice(s) of {plan.slice_elems} elements, "
         f"{plan.held_tiles} tiles held in LDS per workgroup")
     launches = plan.slices  # kernel launches per step (one per slice)
-    main_kernel = (f"mscl_twoshot_held<BF16, {w.nranks}>" if plan.held_tiles
-                   else f"mscl_twoshot<BF16, {w.nranks}, false>")
+    main_kernel = (f"mscl_twoshot_held<BF16, {w.nranks}, {'true' if plan.tile_interleave else 'false'}>"
+                   if plan.held_tiles else f"mscl_twoshot<BF16, {w.nranks}, false>")
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()

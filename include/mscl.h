@@ -117,6 +117,10 @@ typedef struct {
                                 last one shorter), each a complete two-shot; the fields above then
                                 describe the first slice */
   size_t slice_elems;        /* elements per slice (count when slices == 1) */
+  int tile_interleave;       /* sliced held two-shot, R <= 8: 1 when each slice that is a whole number of R
+                                tiles deals its tiles to the ranks in turn (tile T to rank T mod R) instead
+                                of giving each rank one contiguous chunk (a ragged last slice keeps chunks).
+                                MSCL_TILE_INTERLEAVE=0 (environment, read once) turns it off */
 } mscl_plan_t;
 
 /*

@@ -97,8 +97,10 @@ static int run(int R, int dtype, size_t count, int algo, const char* in_path, co
   }
   HIP_OK(hipStreamDestroy(stream));
   free(host);
-  printf("ok R=%d dtype=%d count=%zu algo=%d%s plan_algo=%d cached_puts=%d held_tiles=%d\n", R, dtype, count,
-         algo, in_place ? " in place" : "", (int)plan.algo, plan.cached_puts, plan.held_tiles);
+  printf("ok R=%d dtype=%d count=%zu algo=%d%s plan_algo=%d cached_puts=%d held_tiles=%d slices=%d "
+         "tile_interleave=%d\n",
+         R, dtype, count, algo, in_place ? " in place" : "", (int)plan.algo, plan.cached_puts, plan.held_tiles,
+         plan.slices, plan.tile_interleave);
   return 0;
 }
 

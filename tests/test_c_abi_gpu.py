@@ -32,9 +32,11 @@ CASES = [
 # Plan controls read from the environment once per process, so these run the
 # driver with them set: the put policy forced by MSCL_CACHED_PUTS_MAX_BYTES
 # (streaming puts at sizes whose default is device-scope puts, device-scope
-# puts at a size whose default is streaming), and the two-shot's LDS hold
-# with its default and turned off by MSCL_TWO_SHOT_HOLD=0; (case, environment,
-# what the driver must report about the plan).
+# puts at a size whose default is streaming), the two-shot's LDS hold with
+# its default and turned off by MSCL_TWO_SHOT_HOLD=0, and the interleaved
+# tiles of held slices with their default and turned off by
+# MSCL_TILE_INTERLEAVE=0; (case, environment, what the driver must report
+# about the plan).
 ENV_CASES = [
     ((8, "bf16", 1_000_003, "normal", "two_shot_fused", False), {"MSCL_CACHED_PUTS_MAX_BYTES": "0"}, "cached_puts=0"),
     ((8, "bf16", 1_000_003, "normal", "two_shot", True), {"MSCL_CACHED_PUTS_MAX_BYTES": "0"}, "cached_puts=0"),
@@ -42,6 +44,8 @@ ENV_CASES = [
      "cached_puts=1"),
     ((8, "bf16", 12_000_007, "normal", "auto", False), {}, "held_tiles=23"),
     ((8, "bf16", 12_000_007, "normal", "two_shot", True), {"MSCL_TWO_SHOT_HOLD": "0"}, "held_tiles=0"),
+    ((8, "bf16", 24_000_017, "normal", "two_shot", False), {}, "slices=2 tile_interleave=1"),
+    ((8, "bf16", 24_000_017, "normal", "two_shot", True), {"MSCL_TILE_INTERLEAVE": "0"}, "slices=2 tile_interleave=0"),
 ]
 
 

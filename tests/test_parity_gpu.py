@@ -615,6 +615,11 @@ def test_plan_geometry():
     # device-scope puts while the call's 2*R*S bytes fit in 128 MiB, streaming puts above
     # 128 tiles per workgroup, more than LDS holds: 8 slices of 16 MiB, 16 tiles each
     assert p.cached_puts == 0 and p.slices == 8 and p.slice_elems == (16 << 20) // 2 and p.held_tiles == 16
+    assert p.tile_interleave == 1  # whole-R-tile slices at R <= 8 deal tiles to the ranks in turn
+    q = M.channel_plan(h, (32 << 20) // 2, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.slices == 1 and q.tile_interleave == 0  # a single held launch keeps contiguous chunks
+    q = M.channel_plan(G.channel(16), 64 << 20, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.slices >= 2 and q.tile_interleave == 0  # R = 16 slices keep contiguous chunks
     q = M.channel_plan(h, (32 << 20) // 2, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 32
     mib8 = (8 << 20) // 2
