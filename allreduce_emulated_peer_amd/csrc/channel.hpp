@@ -19,6 +19,9 @@
 //   barrier                          signal, (flush,) wait, then a local
 //                                    workgroup barrier so the other local
 //                                    threads are synchronised too.
+//   per-tile semaphores              a signal per finished tile, so a peer
+//                                    waits only for the tile it needs
+//                                    (TileSemaphores).
 //
 // On one GPU a "peer's memory" is another buffer in the same HBM, reached by
 // ordinary global loads and stores; the rank boundary that matters is the
@@ -57,6 +60,8 @@ struct ChannelArgs {
   uint32_t slots;          // slot stride of inbound / consumed
   int32_t drop_rank;       // test control: this rank skips signal(); -1 = none
   uint64_t timeout_ticks;  // bound of one wait(), in wall-clock ticks (100 MHz)
+  uint32_t* progress;      // [R][slots] per-tile semaphores: tiles each (rank, slot) has finished, all calls
+  uint32_t* seen;          // [R][R][slots] the peer's progress a (rank, slot) had consumed before this call
 };
 
 // What a barrier orders across ranks (see RankChannels::barrier_all).
@@ -170,6 +175,55 @@ struct RankChannels {
     }
     __syncthreads();  // the rest of the workgroup is now synchronised with the peers
     if (kPublishing) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // and sees what they published
+  }
+};
+
+// Per-tile semaphores of slot `slot` of rank `rank`.  Slot b of rank p counts
+// the tiles it has finished in progress[p][b]; the counter only grows.  Slot b
+// of rank r keeps, in seen[r][p][b], how much of peer p's count it had
+// consumed before the current call, so "tile j of this call is ready" is
+// progress - seen >= j + 1 (wrap-safe).  Producer and consumer of a tile are
+// always the same slot of two ranks, so slots whose workgroup count changes
+// between calls stay consistent pairwise, as with the barrier's epochs.
+struct TileSemaphores {
+  const ChannelArgs& ch;
+  int nranks;
+  int rank;
+  int slot;
+
+  __device__ uint32_t* progress_of(int p) const {
+    return ch.progress + static_cast<uint64_t>(p) * ch.slots + slot;
+  }
+  __device__ uint32_t* seen_of(int p) const {
+    return ch.seen + (static_cast<uint64_t>(rank) * nranks + p) * ch.slots + slot;
+  }
+
+  // One more tile of this slot is finished.  The caller has waited for the
+  // tile's device-scope stores to be acknowledged, so the arrival-only
+  // increment already promises the peers that the tile's data is complete.
+  __device__ void signal_tile() const {
+    if (rank == ch.drop_rank) return;
+    __hip_atomic_fetch_add(progress_of(rank), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Tiles of this call peer p's slot has finished (progress - base), polled
+  // until at least `need`.  On running out of time the status records TIMEOUT
+  // and every tile of the peer is reported finished, so the caller waits for
+  // that peer at most once per call (its outputs are then wrong).
+  __device__ uint32_t wait_tiles(int p, uint32_t base, uint32_t need) const {
+    const uint32_t* c = progress_of(p);
+    uint32_t have = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
+    if (static_cast<int32_t>(have - need) >= 0) return have;
+    const uint64_t start = wall_clock64();
+    while (true) {
+      __builtin_amdgcn_s_sleep(1);
+      have = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
+      if (static_cast<int32_t>(have - need) >= 0) return have;
+      if (wall_clock64() - start > ch.timeout_ticks) {
+        __hip_atomic_store(ch.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        return 0x7FFFFFFFu;
+      }
+    }
   }
 };
 

@@ -174,6 +174,33 @@ __device__ inline void store_partial_scoped(void* base, uint64_t vi, const u32x4
   }
 }
 
+// Device-scope loads: what another XCD stored with device scope, read past
+// this XCD's (possibly stale) L2 lines.  Lanes past the resource's range read
+// zero.
+template <int kCpol>
+__device__ inline u32x4 load_vec_scoped(__amdgpu_buffer_rsrc_t rsrc, uint32_t vi) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, vi * 16, 0, kCpol);
+}
+
+// The first `nvalid` (< V) elements of vector `vi` of `base`, loaded element
+// by element with device scope; the rest read as zero bits.
+template <class C, int kCpol>
+__device__ inline u32x4 load_partial_scoped(const void* base, uint64_t vi, int nvalid) {
+  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(const_cast<void*>(base), vi, 1);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if constexpr (C::kElemBytes == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nvalid) v[k] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, 4 * k, 0, kCpol);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nvalid)
+        v[k >> 1] |= static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rsrc, 2 * k, 0, kCpol)) << (16 * (k & 1));
+  }
+  return v;
+}
+
 // First `nvalid` (< V) elements of vector `vi`; the rest read as zero bits.
 template <class C>
 __device__ inline u32x4 load_partial(const void* base, uint64_t vi, int nvalid) {

@@ -697,6 +697,171 @@ __global__ __launch_bounds__(T) void mscl_twoshot_fused(KernelArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Two-shot with per-tile semaphores and a pull (get) all-gather.
+//
+// Reduce-scatter: slot b of rank r reduces its tiles of chunk r, stores each
+// into rank r's own output with device-scope stores and, once they are
+// acknowledged, signals one more finished tile on its per-tile semaphore.
+// All-gather: slot b of rank r then gets, from every peer p's output, the
+// tiles of chunk p that slot b of rank p reduced, each one as soon as that
+// tile's semaphore shows it finished (no barrier between the phases: a tile
+// waits only for its own reduce-scatter), and stores it into its own output.
+// A get is a device-scope load, which reads what the peer's device-scope
+// stores left rather than a stale line of this XCD's L2.  In place, rank r's
+// store into out[r][chunk p] overwrites in[r][chunk p], which only slot b of
+// rank p reads, before it signals that tile.
+// ----------------------------------------------------------------------------
+
+// Slot `slot`'s tiles of a chunk, in the order both phases visit them: its
+// full tiles t = slot, slot + B, ..., then the partial tile if it owns it, then
+// (slot 0) the buffer's partial vector.
+template <class C, int U>
+__device__ inline uint32_t slot_tiles(const Chunk& g, int slot, uint64_t B) {
+  const uint64_t full = static_cast<uint64_t>(slot) < g.nfull_tiles ? (g.nfull_tiles - 1 - slot) / B + 1 : 0;
+  return static_cast<uint32_t>(full + (g.owns_partial_tile ? 1 : 0) + (g.ntail != 0 && slot == 0 ? 1 : 0));
+}
+
+// Wait for the tile's stores, then signal it (whole workgroup).
+__device__ inline void tile_finished(const TileSemaphores& sem) {
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and loads) of the tile, completed
+  __syncthreads();
+  if (threadIdx.x == 0) sem.signal_tile();
+}
+
+template <class C, int R, bool kCachedPuts>
+__global__ __launch_bounds__(kThreads) void mscl_twoshot_pertile(KernelArgs a) {
+  constexpr int U = unroll_for<R>();
+  constexpr uint64_t kTile = static_cast<uint64_t>(kThreads) * U;
+  constexpr int kPutPol = kCachedPuts ? kBufferSc1 : (kBufferSc1 | kBufferNt);
+  const int rank = blockIdx.x % R;
+  const int slot = blockIdx.x / R;
+  const uint64_t B = a.nblk;
+  const uint32_t lane = threadIdx.x;
+  const TileSemaphores sem{a.ch, R, rank, slot};
+  const Chunk g = chunk_of<C, U>(a, rank, slot);
+  void* const mine = a.out[rank];
+
+  // Reduce-scatter into the own output, one signal per tile.  The next tile's
+  // loads are issued before the current tile's stores, so they overlap the
+  // wait for the stores' acknowledgements.
+  if (static_cast<uint64_t>(slot) < g.nfull_tiles) {
+    uint64_t t = slot;
+    u32x4 cur[U][R];
+    load_tile<R, U, true, true>(cur, a.in, g.v_lo + lane + t * kTile, g.v_full);
+    while (true) {
+      const uint64_t tn = t + B;
+      const bool more = tn < g.nfull_tiles;
+      u32x4 nxt[U][R];
+      if (more) load_tile<R, U, true, true>(nxt, a.in, g.v_lo + lane + tn * kTile, g.v_full);
+      u32x4 y[U];
+      reduce_tile<C, R, U>(y, cur);
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(mine, g.v_lo + t * kTile, kTile);
+#pragma unroll
+      for (int u = 0; u < U; ++u) store_vec_scoped<kBufferSc1>(rs, lane + static_cast<uint32_t>(u * kThreads), y[u]);
+      tile_finished(sem);
+      if (!more) break;
+      for (int u = 0; u < U; ++u)
+        for (int p = 0; p < R; ++p) cur[u][p] = nxt[u][p];
+      t = tn;
+    }
+  }
+  if (g.owns_partial_tile) {
+    u32x4 x[U][R];
+    u32x4 y[U];
+    const uint64_t v0 = g.v_lo + g.nfull_tiles * kTile;
+    load_tile<R, U, false, true>(x, a.in, v0 + lane, g.v_full);
+    reduce_tile<C, R, U>(y, x);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(mine, v0, g.v_full - v0);  // lanes past the chunk are dropped
+#pragma unroll
+    for (int u = 0; u < U; ++u) store_vec_scoped<kBufferSc1>(rs, lane + static_cast<uint32_t>(u * kThreads), y[u]);
+    tile_finished(sem);
+  }
+  if (g.ntail != 0 && slot == 0) {
+    if (lane == 0) store_partial_scoped<C, kBufferSc1>(mine, g.v_full, reduce_partial<C, R>(a, g.v_full, g.ntail), g.ntail);
+    tile_finished(sem);
+  }
+
+  // All-gather by get: the same slot's tiles of every peer's chunk, each as
+  // soon as its semaphore shows it finished.  The tiles go in columns: step j
+  // gets tile j of every peer's chunk, all loads issued before any store, so
+  // up to R - 1 loads per lane are in flight.  ready_sh[p] caches how many
+  // of peer p's tiles are known finished (first from one read of every
+  // peer's semaphore, lane p of wave 0 reading peer p's), so a semaphore is
+  // polled again only when the tile needed next is not yet known finished.
+  __shared__ uint32_t base_sh[kMaxRanks], ready_sh[kMaxRanks], nvec_sh[kMaxRanks];
+  if (lane < static_cast<uint32_t>(R)) {
+    const int p = static_cast<int>(lane);
+    const Chunk gp = chunk_of<C, U>(a, p, slot);
+    const uint64_t nfull_mine = static_cast<uint64_t>(slot) < gp.nfull_tiles ? (gp.nfull_tiles - 1 - slot) / B + 1 : 0;
+    nvec_sh[p] = p == rank ? 0u : static_cast<uint32_t>(nfull_mine + (gp.owns_partial_tile ? 1 : 0));
+    const uint32_t b0 = __hip_atomic_load(sem.seen_of(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    base_sh[p] = b0;
+    const uint32_t have =
+        p == rank ? 0u : __hip_atomic_load(sem.progress_of(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - b0;
+    ready_sh[p] = static_cast<int32_t>(have) > 0 ? have : 0u;
+  }
+  __syncthreads();
+  uint32_t columns = 0;
+#pragma unroll
+  for (int p = 0; p < R; ++p) columns = std::max(columns, nvec_sh[p]);
+  for (uint32_t j = 0; j < columns; ++j) {
+    if (lane == 0) {
+      for (int k = 1; k < R; ++k) {
+        const int p = (rank + k) % R;
+        if (j < nvec_sh[p] && j >= ready_sh[p]) ready_sh[p] = sem.wait_tiles(p, base_sh[p], j + 1);
+      }
+    }
+    __syncthreads();
+    u32x4 y[R][U];
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+      if (p != rank && j < nvec_sh[p]) {
+        const Chunk gp = chunk_of<C, U>(a, p, slot);
+        const uint64_t nfull_mine = (gp.nfull_tiles - 1 - slot) / B + 1;  // j < nvec implies slot has a tile
+        const uint64_t t = static_cast<uint64_t>(slot) < gp.nfull_tiles && j < nfull_mine ? slot + j * B
+                                                                                         : gp.nfull_tiles;
+        const uint64_t v0 = gp.v_lo + t * kTile;
+        const uint64_t nv = std::min<uint64_t>(kTile, gp.v_full - v0);  // lanes past it read zero
+        const __amdgpu_buffer_rsrc_t src = tile_rsrc(a.out[p], v0, nv);
+#pragma unroll
+        for (int u = 0; u < U; ++u) y[p][u] = load_vec_scoped<kBufferSc1>(src, lane + static_cast<uint32_t>(u * kThreads));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+      if (p != rank && j < nvec_sh[p]) {
+        const Chunk gp = chunk_of<C, U>(a, p, slot);
+        const uint64_t nfull_mine = (gp.nfull_tiles - 1 - slot) / B + 1;
+        const uint64_t t = static_cast<uint64_t>(slot) < gp.nfull_tiles && j < nfull_mine ? slot + j * B
+                                                                                         : gp.nfull_tiles;
+        const uint64_t v0 = gp.v_lo + t * kTile;
+        const uint64_t nv = std::min<uint64_t>(kTile, gp.v_full - v0);  // lanes past it store nothing
+        const __amdgpu_buffer_rsrc_t dst = tile_rsrc(mine, v0, nv);
+#pragma unroll
+        for (int u = 0; u < U; ++u) store_vec_scoped<kPutPol>(dst, lane + static_cast<uint32_t>(u * kThreads), y[p][u]);
+      }
+    }
+  }
+  // The buffer's partial vector, the last item of slot 0 of the chunk that
+  // holds the buffer's end.
+  if (slot == 0 && lane == 0) {
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+      if (p == rank) continue;
+      const Chunk gp = chunk_of<C, U>(a, p, slot);
+      if (gp.ntail == 0) continue;
+      if (ready_sh[p] < nvec_sh[p] + 1) sem.wait_tiles(p, base_sh[p], nvec_sh[p] + 1);
+      store_partial<C>(mine, gp.v_full, load_partial_scoped<C, kBufferSc1>(a.out[p], gp.v_full, gp.ntail), gp.ntail);
+    }
+  }
+  if (lane < static_cast<uint32_t>(R) && static_cast<int>(lane) != rank) {
+    const Chunk gp = chunk_of<C, U>(a, static_cast<int>(lane), slot);
+    __hip_atomic_store(sem.seen_of(static_cast<int>(lane)), base_sh[lane] + slot_tiles<C, U>(gp, slot, B),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// ----------------------------------------------------------------------------
 // ReduceScatter and AllGather: the two halves of the two-shot as standard
 // collectives of their own (the pages' library implements the standard
 // collective API; MSCCL++ ASPLOS'26 abstract).
@@ -923,7 +1088,9 @@ enum {
   kAlgoTwoShotFusedHalfSync = 15,
   kAlgoTwoShotFusedCachedPutsSync = 16,
   kAlgoTwoShotFusedHalfCachedPutsSync = 17,
-  kAlgoTwoShotHeldInterleaved = 18  // the held two-shot with tiles dealt to the ranks in turn
+  kAlgoTwoShotHeldInterleaved = 18,  // the held two-shot with tiles dealt to the ranks in turn
+  kAlgoTwoShotPerTile = 19,          // per-tile semaphores, pull all-gather (streaming / device-scope puts)
+  kAlgoTwoShotPerTileCachedPuts = 20
 };
 
 template <class C, int R>
@@ -943,6 +1110,8 @@ constexpr KernelFn kernel_for(int kind) {
     case kAlgoTwoShotFusedHalfCachedPutsSync: return &mscl_twoshot_fused<C, R, kThreads / 2, true, true>;
     case kAlgoTwoShotHeld: return &mscl_twoshot_held<C, R, false>;
     case kAlgoTwoShotHeldInterleaved: return &mscl_twoshot_held<C, R, true>;
+    case kAlgoTwoShotPerTile: return &mscl_twoshot_pertile<C, R, false>;
+    case kAlgoTwoShotPerTileCachedPuts: return &mscl_twoshot_pertile<C, R, true>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;
     case kReduceScatterElem: return &mscl_reduce_scatter_kernel<C, R, false>;
     case kAllGatherVec: return &mscl_allgather_kernel<C, R, true>;

@@ -20,12 +20,12 @@
 #include "kernels.hpp"
 #include "port_proxy.hpp"
 
-// Channel state of mscl_allreduce_noalloc (see there): 64 KiB of device
+// Channel state of mscl_allreduce_noalloc (see there): 128 KiB of device
 // memory in the library's code object, one copy per device the library runs
 // on, held until the process ends.  Host code never passes this name to a
 // kernel (on the host it is only a stand-in for the symbol): it uses the
 // address hipGetSymbolAddress returns for the current device.
-constexpr size_t kScratchWords = (size_t(64) << 10) / sizeof(uint32_t);
+constexpr size_t kScratchWords = (size_t(128) << 10) / sizeof(uint32_t);
 static __device__ __align__(256) uint32_t scratch[kScratchWords];
 
 // ----------------------------------------------------------------------------
@@ -62,7 +62,7 @@ size_t elem_bytes(int dtype) { return dtype == MSCL_FLOAT32 ? 4 : 2; }
 bool valid_algo(int algo) {
   return algo == MSCL_ALGO_AUTO || algo == MSCL_ALGO_ONE_SHOT || algo == MSCL_ALGO_TWO_SHOT ||
          algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_PORT ||
-         algo == MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER;
+         algo == MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER || algo == MSCL_ALGO_TWO_SHOT_PERTILE;
 }
 
 bool is_fused(int algo) { return algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER;
@@ -114,6 +114,7 @@ const char* algo_name(int algo) {
     case MSCL_ALGO_TWO_SHOT_FUSED: return "two_shot_fused";
     case MSCL_ALGO_TWO_SHOT_PORT: return "two_shot_port";
     case MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER: return "two_shot_fused_nobarrier";
+    case MSCL_ALGO_TWO_SHOT_PERTILE: return "two_shot_pertile";
   }
   return "?";
 }
@@ -128,8 +129,8 @@ struct mscl_channel_s {
   uint32_t slots = 0;            // barrier slots allocated per rank (= max co-resident workgroups per rank)
   uint32_t held_slots = 0;       // the same bound for the two-shot that keeps tiles in LDS (one per CU)
   uint64_t wall_clock_khz = 100000;
-  uint32_t* inbound = nullptr;   // device [R][R][slots]
-  uint32_t* consumed = nullptr;  // device [R][slots]
+  uint32_t* inbound = nullptr;   // device [R][R][slots] barrier counters, then [R][R][slots] per-tile `seen`
+  uint32_t* consumed = nullptr;  // device [R][slots] consumed signals, then [R][slots] per-tile `progress`
   int* status_host = nullptr;    // host-mapped status word
   int* status_dev = nullptr;
   uint64_t wait_timeout_us = 0;  // 0 = config default
@@ -284,7 +285,7 @@ constexpr size_t kCachedPutsMaxFootprint = size_t(128) << 20;
 // 49.0 us; R = 8, 16 MiB, 16 tiles, 44.3 -> 43.3 us).
 constexpr uint64_t kHeldMinTiles = 16;
 bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
-  if (algo != MSCL_ALGO_TWO_SHOT && !is_fused(algo)) return false;
+  if (algo != MSCL_ALGO_TWO_SHOT && algo != MSCL_ALGO_TWO_SHOT_PERTILE && !is_fused(algo)) return false;
   if (bytes > (size_t(1) << 31)) return false;  // the two-shot's buffer store takes a 32-bit byte range
   const size_t env = config().cached_puts_max_footprint;
   const size_t limit = env != SIZE_MAX ? env : kCachedPutsMaxFootprint;
@@ -304,7 +305,8 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   plan->vectors_per_thread = unroll_for_runtime(R);
   plan->cached_puts = cached_puts(algo, R, count * elem_bytes(dtype)) ? 1 : 0;
   uint64_t vectors;  // full vectors one rank covers
-  if (algo == MSCL_ALGO_TWO_SHOT || is_fused(algo) || algo == MSCL_ALGO_TWO_SHOT_PORT) {
+  if (algo == MSCL_ALGO_TWO_SHOT || is_fused(algo) || algo == MSCL_ALGO_TWO_SHOT_PORT ||
+      algo == MSCL_ALGO_TWO_SHOT_PERTILE) {
     const uint64_t per = (count + R - 1) / R;
     // Chunks are whole 16-byte vectors; from 32 pages of 4 KiB per rank up,
     // whole 4 KiB pages, so that every rank's chunk starts where its tiles
@@ -318,7 +320,8 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
     const uint64_t c = (per + align - 1) / align * align;
     plan->chunk_elems = c;
     vectors = c / V;
-    plan->uses_barrier = (algo == MSCL_ALGO_TWO_SHOT || algo == MSCL_ALGO_TWO_SHOT_FUSED) ? 1 : 0;
+    plan->uses_barrier =
+        (algo == MSCL_ALGO_TWO_SHOT || algo == MSCL_ALGO_TWO_SHOT_FUSED || algo == MSCL_ALGO_TWO_SHOT_PERTILE) ? 1 : 0;
   } else {
     vectors = count / V;
     plan->uses_barrier = in_place ? 1 : 0;
@@ -444,6 +447,8 @@ void fill_args(KernelArgs* a, const Bound& b, const void* const inputs[], void* 
   a->count = count;
   a->ch.inbound = b.ch->inbound;
   a->ch.consumed = b.ch->consumed;
+  a->ch.seen = b.ch->inbound + static_cast<size_t>(nranks) * nranks * b.ch->slots;
+  a->ch.progress = b.ch->consumed + static_cast<size_t>(nranks) * b.ch->slots;
   a->ch.status = b.ch->status_dev;
   a->ch.slots = b.ch->slots;
   a->ch.drop_rank = b.drop_rank;
@@ -539,7 +544,8 @@ hipError_t barrier_slots(int nranks, int cus, uint32_t* slots, uint32_t* held_sl
   int min_resident = 1 << 30;
   for (int dt = 0; dt < 3; ++dt) {
     for (int kind : {kAlgoOneShotInPlace, kAlgoTwoShot, kAlgoTwoShotCachedPuts, kAlgoTwoShotFusedSync,
-                     kAlgoTwoShotFusedCachedPutsSync, kAlgoTwoShotFusedHalfSync, kAlgoTwoShotFusedHalfCachedPutsSync}) {
+                     kAlgoTwoShotFusedCachedPutsSync, kAlgoTwoShotFusedHalfSync, kAlgoTwoShotFusedHalfCachedPutsSync,
+                     kAlgoTwoShotPerTile, kAlgoTwoShotPerTileCachedPuts}) {
       int per_cu = 0;
       const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)), threads_for_kind(kind), 0);
@@ -577,6 +583,8 @@ int kind_for(const mscl_plan_t& plan, bool in_place) {
                   : (cached ? kAlgoTwoShotFusedHalfCachedPuts : kAlgoTwoShotFusedHalf);
     case MSCL_ALGO_TWO_SHOT_PORT:
       return kAlgoTwoShotPort;
+    case MSCL_ALGO_TWO_SHOT_PERTILE:
+      return cached ? kAlgoTwoShotPerTileCachedPuts : kAlgoTwoShotPerTile;
     default:
       return in_place ? kAlgoOneShotInPlace : kAlgoOneShot;
   }
@@ -627,8 +635,9 @@ mscl_status_t launch_allreduce(const mscl_channel_s* ch, const KernelArgs& proto
 // Allocation-free AllReduce (mscl_allreduce_noalloc): the channel state lives
 // in `scratch`, a device array of the library's own code object, so the call
 // allocates nothing.  Layout for R ranks and a slot stride S (per device and
-// R): inbound [R][R][S] counters, consumed [R][S] counters, then the status
-// word.  Each call clears the words it uses (a fill kernel on the stream: no
+// R): inbound [R][R][S] counters, the per-tile semaphores' seen [R][R][S],
+// consumed [R][S] counters, the per-tile semaphores' progress [R][S], then the
+// status word.  Each call clears the words it uses (a fill kernel on the stream: no
 // memset node in a captured graph) before its barrier kernels run, so a call
 // never inherits the counters of an earlier one.
 // ----------------------------------------------------------------------------
@@ -681,7 +690,8 @@ mscl_status_t noalloc_geometry(int device, int nranks, NoAllocDevice* out) {
     // No launch has more than two workgroups per compute unit in total, so
     // that bounds the stride too; then it must fit the array.
     const uint32_t widest = static_cast<uint32_t>(std::max(1, 2 * d.cus / nranks));
-    const uint32_t fits = static_cast<uint32_t>((kScratchWords - 1) / (static_cast<size_t>(nranks) * nranks + nranks));
+    const uint32_t fits =
+        static_cast<uint32_t>((kScratchWords - 1) / (2 * (static_cast<size_t>(nranks) * nranks + nranks)));
     slots = std::min({slots, widest, fits});
     if (slots == 0) return fail(MSCL_ERR_INVALID_ARGUMENT, "the scratch array cannot hold one barrier slot per rank");
     d.held_slots[nranks] = std::min(held, slots);
@@ -768,8 +778,10 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
     (void)hipSetDevice(prev);
     return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   }
-  const size_t inbound_bytes = sizeof(uint32_t) * nranks * nranks * ch->slots;
-  const size_t consumed_bytes = sizeof(uint32_t) * nranks * ch->slots;
+  // Each array holds the barrier's counters followed by the per-tile
+  // semaphores' (seen after inbound, progress after consumed).
+  const size_t inbound_bytes = 2 * sizeof(uint32_t) * nranks * nranks * ch->slots;
+  const size_t consumed_bytes = 2 * sizeof(uint32_t) * nranks * ch->slots;
   mscl_status_t st = MSCL_SUCCESS;
   if ((e = hipMalloc(&ch->inbound, inbound_bytes)) != hipSuccess ||
       (e = hipMalloc(&ch->consumed, consumed_bytes)) != hipSuccess) {
@@ -835,8 +847,8 @@ mscl_status_t mscl_channel_reset(mscl_channel_t ch) {
   (void)hipSetDevice(ch->device);
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = port_reset(ch);
-  if (e == hipSuccess) e = hipMemset(ch->inbound, 0, sizeof(uint32_t) * ch->nranks * ch->nranks * ch->slots);
-  if (e == hipSuccess) e = hipMemset(ch->consumed, 0, sizeof(uint32_t) * ch->nranks * ch->slots);
+  if (e == hipSuccess) e = hipMemset(ch->inbound, 0, 2 * sizeof(uint32_t) * ch->nranks * ch->nranks * ch->slots);
+  if (e == hipSuccess) e = hipMemset(ch->consumed, 0, 2 * sizeof(uint32_t) * ch->nranks * ch->slots);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail_hip(e, "resetting channel state");
@@ -917,12 +929,15 @@ mscl_status_t mscl_allreduce_noalloc(const void* const inputs[], void* const out
   mscl_plan_t plan;
   make_plan(&geom, count, dtype, resolved, in_place, &plan);
   const uint32_t stride = geom.slots;
-  uint32_t words = static_cast<uint32_t>(static_cast<size_t>(nranks) * nranks * stride + nranks * stride + 1);
-  if (words > kScratchWords) return fail(MSCL_ERR_INVALID_ARGUMENT, "channel state exceeds the 64 KiB scratch array");
+  const size_t pair = static_cast<size_t>(nranks) * nranks * stride, own = static_cast<size_t>(nranks) * stride;
+  uint32_t words = static_cast<uint32_t>(2 * pair + 2 * own + 1);
+  if (words > kScratchWords) return fail(MSCL_ERR_INVALID_ARGUMENT, "channel state exceeds the 128 KiB scratch array");
   KernelArgs a;
   memset(&a, 0, sizeof(a));
   a.ch.inbound = d.scratch;
-  a.ch.consumed = d.scratch + static_cast<size_t>(nranks) * nranks * stride;
+  a.ch.seen = d.scratch + pair;
+  a.ch.consumed = d.scratch + 2 * pair;
+  a.ch.progress = d.scratch + 2 * pair + own;
   a.ch.status = reinterpret_cast<int*>(d.scratch + words - 1);
   a.ch.slots = stride;
   a.ch.drop_rank = -1;

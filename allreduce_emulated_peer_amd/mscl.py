@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libmscl.so")
 FLOAT32, FLOAT16, BFLOAT16 = 0, 1, 2
 ALGO_AUTO, ALGO_ONE_SHOT, ALGO_TWO_SHOT, ALGO_TWO_SHOT_FUSED, ALGO_TWO_SHOT_PORT = 0, 1, 2, 3, 4
 ALGO_TWO_SHOT_FUSED_NOBARRIER = 5
+ALGO_TWO_SHOT_PERTILE = 6
 MAX_RANKS = 16
 
 SUCCESS = 0
@@ -35,7 +36,7 @@ ERR_TIMEOUT = 7
 DTYPE_CODES = {"fp32": FLOAT32, "fp16": FLOAT16, "bf16": BFLOAT16}
 ALGO_CODES = {"auto": ALGO_AUTO, "one_shot": ALGO_ONE_SHOT, "two_shot": ALGO_TWO_SHOT,
               "two_shot_fused": ALGO_TWO_SHOT_FUSED, "two_shot_port": ALGO_TWO_SHOT_PORT,
-              "two_shot_fused_nobarrier": ALGO_TWO_SHOT_FUSED_NOBARRIER}
+              "two_shot_fused_nobarrier": ALGO_TWO_SHOT_FUSED_NOBARRIER, "two_shot_pertile": ALGO_TWO_SHOT_PERTILE}
 
 # every function include/mscl.h declares
 EXPORTS = (

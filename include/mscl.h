@@ -75,11 +75,16 @@ typedef enum {
                                    requests to a host proxy thread, which copies them with the
                                    SDMA engines, and waits for their completion.  Never chosen
                                    by AUTO (see mscl_allreduce) */
-  MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER = 5 /* MSCL_ALGO_TWO_SHOT_FUSED without the completion
+  MSCL_ALGO_TWO_SHOT_FUSED_NOBARRIER = 5, /* MSCL_ALGO_TWO_SHOT_FUSED without the completion
                                    barrier: no signal or wait at all; completion is the end of
                                    the kernel on the stream, which covers every rank only
                                    because all ranks share one GPU.  A comparison variant,
                                    never chosen by AUTO */
+  MSCL_ALGO_TWO_SHOT_PERTILE = 6 /* reduce-scatter into each rank's own output with a semaphore
+                                   signal per finished tile, then an all-gather in which every
+                                   rank gets each peer's reduced tiles from the peer's output,
+                                   each tile as soon as its semaphore shows it finished (no
+                                   barrier between the phases).  Never chosen by AUTO */
 } mscl_algo_t;
 
 typedef int mscl_status_t;
@@ -224,8 +229,9 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  *   dtype   : element type of inputs and outputs.
  *   nranks  : R, 1..MSCL_MAX_RANKS; a channel set for (current device, R)
  *             must exist (mscl_channel_create).
- *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT, _TWO_SHOT, _TWO_SHOT_FUSED or
- *             _TWO_SHOT_PORT.  All give bit-identical results.
+ *   algo    : MSCL_ALGO_AUTO, _ONE_SHOT, _TWO_SHOT, _TWO_SHOT_FUSED,
+ *             _TWO_SHOT_PORT, _TWO_SHOT_FUSED_NOBARRIER or _TWO_SHOT_PERTILE.
+ *             All give bit-identical results.
  *   stream  : hipStream_t on the current device (NULL = default stream).
  * Every pointer must be 16-byte aligned and on the current device.  The call
  * is asynchronous: it validates, launches one kernel on `stream` (one per
@@ -249,6 +255,11 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * Infinity Cache for the kernel that reads them next; above that they
  * stream past the caches (mscl_channel_plan reports the choice).  It
  * changes time only, never results.
+ * MSCL_ALGO_TWO_SHOT_PERTILE uses the channels' get (read the peer's memory
+ * directly) and a semaphore per tile instead of one barrier (MSCCL++
+ * README, Key Concepts, "On-GPU Communication Interfaces: Channels": put,
+ * get, signal, wait); it moves about (3R - 1) * S bytes, against 2R * S
+ * for the held two-shot, so AUTO does not use it.
  * MSCL_ALGO_TWO_SHOT_PORT follows the pages' PortChannel (MSCCL++ README, Key
  * Concepts, "PortChannel and MemoryChannel", "Host-Side Communication
  * Proxy"): GPU threads only post requests, and a CPU proxy moves the data
@@ -272,7 +283,7 @@ mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], 
  * the same arguments, algorithms and results, but no channel set is needed
  * and nothing is allocated, neither at the first call nor later.  The
  * channel state (semaphores, consumed-signal counters, status word) lives in
- * a 64 KiB array in the library's device code, one per device, held until
+ * a 128 KiB array in the library's device code, one per device, held until
  * the process ends; the first call on a device looks up that array's address
  * and the device's geometry (host queries only).  Every call clears the
  * words its barriers use (a fill kernel on `stream`, no memset) before it

@@ -21,8 +21,8 @@ TORCH_DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bflo
 CODES = {"fp32": M.FLOAT32, "fp16": M.FLOAT16, "bf16": M.BFLOAT16}
 ALGOS = {"one_shot": M.ALGO_ONE_SHOT, "two_shot": M.ALGO_TWO_SHOT, "two_shot_fused": M.ALGO_TWO_SHOT_FUSED,
          "two_shot_port": M.ALGO_TWO_SHOT_PORT, "two_shot_fused_nobarrier": M.ALGO_TWO_SHOT_FUSED_NOBARRIER,
-         "auto": M.ALGO_AUTO}
-EXPLICIT = ("one_shot", "two_shot", "two_shot_fused", "two_shot_port", "two_shot_fused_nobarrier")
+         "two_shot_pertile": M.ALGO_TWO_SHOT_PERTILE, "auto": M.ALGO_AUTO}
+EXPLICIT = ("one_shot", "two_shot", "two_shot_fused", "two_shot_port", "two_shot_fused_nobarrier", "two_shot_pertile")
 POISON = 0xA5
 
 _channels = {}

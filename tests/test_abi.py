@@ -63,7 +63,7 @@ def test_bad_nranks(R):
 def test_bad_dtype_and_algo():
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 3, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, -1, 2, 0, 0) == M.ERR_INVALID_ARGUMENT
-    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 6, 0) == M.ERR_INVALID_ARGUMENT
+    assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, 7, 0) == M.ERR_INVALID_ARGUMENT
     assert M.raw_allreduce(addrs(2, A), addrs(2, A * 64), 10, 0, 2, -1, 0) == M.ERR_INVALID_ARGUMENT
 
 

@@ -269,9 +269,10 @@ def test_repeated_calls_keep_epochs():
     outs = [G.poison_like(t) for t in ins]
     h = G.channel(R)
     stream = torch.cuda.current_stream().cuda_stream
-    G.note("10^4 repeated one-shot / two-shot / fused two-shot / port two-shot calls")
+    G.note("10^4 repeated one-shot / two-shot / fused two-shot / port two-shot / per-tile two-shot calls")
     for i in range(10_000):
-        algo = (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT)[i % 4]
+        algo = (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT,
+                M.ALGO_TWO_SHOT_PERTILE)[i % 5]
         M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, R, algo, stream)
         if i % 1000 == 999:
             torch.cuda.synchronize()
@@ -298,7 +299,7 @@ def test_graph_capture_and_replay():
     ins = [G.to_device(x, "bf16") for x in xs]
     G.channel(R)
     for algo in (M.ALGO_TWO_SHOT, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PORT,
-                 M.ALGO_TWO_SHOT_FUSED_NOBARRIER):
+                 M.ALGO_TWO_SHOT_FUSED_NOBARRIER, M.ALGO_TWO_SHOT_PERTILE):
         outs = [G.poison_like(t) for t in ins]
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -371,15 +372,16 @@ def test_graph_capture_of_held_and_sliced_two_shots():
 
 @pytest.mark.parametrize("algo,in_place", [(M.ALGO_TWO_SHOT, False), (M.ALGO_ONE_SHOT, True),
                                            (M.ALGO_TWO_SHOT_PORT, False), (M.ALGO_TWO_SHOT_FUSED, False),
-                                           (M.ALGO_TWO_SHOT_FUSED, True)])
+                                           (M.ALGO_TWO_SHOT_FUSED, True), (M.ALGO_TWO_SHOT_PERTILE, False),
+                                           (M.ALGO_TWO_SHOT_PERTILE, True)])
 def test_timeout_is_reported_not_hung(algo, in_place):
     """Force a missing signal from the host (rank 1 skips signal(), or with
     the port channel posts no puts) with a 2 ms bound on every wait(): the
     kernel must exit, the status must read TIMEOUT, further calls must refuse
     until reset, and a reset must bring the channel back.  The two-shot's
     arrival-only barrier, the in-place one-shot's after-reads barrier, the
-    port channel's wait for the proxy, and the fused two-shot's completion
-    barrier."""
+    port channel's wait for the proxy, the fused two-shot's completion
+    barrier and the per-tile semaphores."""
     R, n = 4, 100_000
     xs = P.rand_inputs(R, n, "fp32", seed=31)
     want = O.allreduce(xs, "fp32")
@@ -401,7 +403,7 @@ def test_timeout_is_reported_not_hung(algo, in_place):
         M.channel_reset(h)
     assert M.channel_check(h) == M.SUCCESS
     names = {M.ALGO_TWO_SHOT: "two_shot", M.ALGO_ONE_SHOT: "one_shot", M.ALGO_TWO_SHOT_PORT: "two_shot_port",
-             M.ALGO_TWO_SHOT_FUSED: "two_shot_fused"}
+             M.ALGO_TWO_SHOT_FUSED: "two_shot_fused", M.ALGO_TWO_SHOT_PERTILE: "two_shot_pertile"}
     outs = G.run(xs, "fp32", names[algo], in_place=in_place)
     G.assert_matches_oracle(outs, want, "fp32", "after reset")
 

@@ -42,7 +42,8 @@ def _both(R, n, dtype, algo, in_place, seed):
     return outs_a, outs_b
 
 
-@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused", "two_shot_fused_nobarrier"])
+@pytest.mark.parametrize("algo", ["auto", "one_shot", "two_shot", "two_shot_fused", "two_shot_fused_nobarrier",
+                                  "two_shot_pertile"])
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("R,dtype,sizes", [(8, "bf16", (24_000_017, 300_001)), (16, "fp16", (9_000_011, 777)),
                                            (4, "fp32", (3_000_017, 70_001))],
