@@ -528,11 +528,14 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
 // slices of large calls at R <= 8 (R = 8, 128 MiB in 8 slices: 347.8 ->
 // 340.9 us; 64 MiB in 4 slices: 173.5 -> 168.8 us; it loses on single held
 // launches and at R = 16).
-template <class C, int R, bool kIlv>
+//
+// kCachedPuts: device-scope temporal puts (the host's choice while the call's
+// 2*R*S bytes fit the Infinity Cache), else streaming puts.
+template <class C, int R, bool kIlv, bool kCachedPuts = false>
 __global__ __launch_bounds__(kThreads) void mscl_twoshot_held(KernelArgs a) {
   if constexpr (unroll_for<R>() == 1) {
     __shared__ u32x4 held[kHeldTiles][kThreads];
-    twoshot_body<C, R, false, true, kIlv>(a, held);
+    twoshot_body<C, R, kCachedPuts, true, kIlv>(a, held);
   } else {
     twoshot_body<C, R, false, false>(a, nullptr);  // several vectors per lane: the host never picks this
   }
@@ -1090,7 +1093,8 @@ enum {
   kAlgoTwoShotFusedHalfCachedPutsSync = 17,
   kAlgoTwoShotHeldInterleaved = 18,  // the held two-shot with tiles dealt to the ranks in turn
   kAlgoTwoShotPerTile = 19,          // per-tile semaphores, pull all-gather (streaming / device-scope puts)
-  kAlgoTwoShotPerTileCachedPuts = 20
+  kAlgoTwoShotPerTileCachedPuts = 20,
+  kAlgoTwoShotHeldCachedPuts = 21  // the held two-shot with device-scope temporal puts
 };
 
 template <class C, int R>
@@ -1110,6 +1114,7 @@ constexpr KernelFn kernel_for(int kind) {
     case kAlgoTwoShotFusedHalfCachedPutsSync: return &mscl_twoshot_fused<C, R, kThreads / 2, true, true>;
     case kAlgoTwoShotHeld: return &mscl_twoshot_held<C, R, false>;
     case kAlgoTwoShotHeldInterleaved: return &mscl_twoshot_held<C, R, true>;
+    case kAlgoTwoShotHeldCachedPuts: return &mscl_twoshot_held<C, R, false, true>;
     case kAlgoTwoShotPerTile: return &mscl_twoshot_pertile<C, R, false>;
     case kAlgoTwoShotPerTileCachedPuts: return &mscl_twoshot_pertile<C, R, true>;
     case kReduceScatterVec: return &mscl_reduce_scatter_kernel<C, R, true>;

@@ -279,6 +279,20 @@ mscl_algo_t resolve_algo(size_t count, int dtype, int nranks, int algo, bool in_
 // cached pay 10-20% (two-shot R = 8 16 MiB 42.7 -> 51.1).
 constexpr size_t kCachedPutsMaxFootprint = size_t(128) << 20;
 
+// The held two-shot writes its outputs in a pure write phase, and there
+// device-scope puts pay up to a 256 MiB footprint: R = 8, 16 MiB, streaming ->
+// device-scope puts, 42.3 -> 38.7 us on the same buffers, 40.4 -> 32.6 us
+// between a producer and a consumer kernel, 43.1 -> 43.0 us over four rotated
+// buffer sets; at 512 MiB they lose between a producer and a consumer (R = 8,
+// 32 MiB: 81.1 -> 92.7 us; R = 16, 16 MiB: 91.7 -> 97.0 us).
+constexpr size_t kHeldCachedPutsMaxFootprint = size_t(256) << 20;
+bool held_cached_puts(int nranks, size_t bytes) {
+  if (bytes > (size_t(1) << 31)) return false;
+  const size_t env = config().cached_puts_max_footprint;
+  const size_t limit = env != SIZE_MAX ? env : kHeldCachedPutsMaxFootprint;
+  return 2 * static_cast<size_t>(nranks) * bytes <= limit;
+}
+
 // Fewest full tiles per workgroup for which the held two-shot pays (below, its
 // all-gather's store of the held tiles to the rank's own output costs more
 // than the skipped store and re-read save: R = 16, 8 MiB, 8 tiles, 47.7 ->
@@ -361,11 +375,12 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   // and 7 gain 8-13% sliced at 64-128 MiB: R = 7, 128 MiB, 404 -> 350 us).
   plan->slices = 1;
   plan->slice_elems = count;
-  if (algo == MSCL_ALGO_TWO_SHOT && !plan->cached_puts && cfg.two_shot_hold && plan->vectors_per_thread == 1 &&
-      R >= 6 && b <= ch->held_slots) {
+  if (algo == MSCL_ALGO_TWO_SHOT && cfg.two_shot_hold && plan->vectors_per_thread == 1 && R >= 6 &&
+      b <= ch->held_slots) {
     const uint64_t per_slot = (vectors / tile + b - 1) / b;  // full tiles of the busiest workgroup
     if (per_slot >= kHeldMinTiles && per_slot <= static_cast<uint64_t>(kHeldTiles)) {
       plan->held_tiles = static_cast<int>(per_slot);
+      plan->cached_puts = held_cached_puts(R, count * elem_bytes(dtype)) ? 1 : 0;
     } else if (per_slot > static_cast<uint64_t>(kHeldTiles) && allow_slices) {
       // Too large to hold: run the call as consecutive slices, each a
       // complete two-shot whose shares fit in LDS.  Slice boundaries keep
@@ -390,6 +405,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
         *plan = first;
         plan->slice_elems = m;
         plan->slices = static_cast<int>((count + m - 1) / m);
+        plan->cached_puts = held_cached_puts(R, count * elem_bytes(dtype)) ? 1 : 0;  // the whole call's footprint
         // Slices that are a whole number of R tiles (all but a ragged last one:
         // m is a multiple of R tiles) deal their tiles to the ranks in turn, so
         // that at any moment every workgroup reads and writes one neighbourhood
@@ -557,7 +573,7 @@ hipError_t barrier_slots(int nranks, int cus, uint32_t* slots, uint32_t* held_sl
   int held_resident = 1 << 30;
   for (int dt = 0; dt < 3; ++dt) {
     int per_cu = 0;
-    for (int kind : {kAlgoTwoShotHeld, kAlgoTwoShotHeldInterleaved}) {
+    for (int kind : {kAlgoTwoShotHeld, kAlgoTwoShotHeldInterleaved, kAlgoTwoShotHeldCachedPuts}) {
       const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, reinterpret_cast<const void*>(kernel_lookup(kind, dt, nranks)), kThreads, 0);
       if (e != hipSuccess) return e;
@@ -574,7 +590,8 @@ int kind_for(const mscl_plan_t& plan, bool in_place) {
   const bool wide = plan.threads_per_workgroup == kThreads;
   switch (plan.algo) {
     case MSCL_ALGO_TWO_SHOT:
-      return plan.held_tiles ? kAlgoTwoShotHeld : cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot;
+      if (plan.held_tiles) return cached ? kAlgoTwoShotHeldCachedPuts : kAlgoTwoShotHeld;
+      return cached ? kAlgoTwoShotCachedPuts : kAlgoTwoShot;
     case MSCL_ALGO_TWO_SHOT_FUSED:
       return wide ? (cached ? kAlgoTwoShotFusedCachedPutsSync : kAlgoTwoShotFusedSync)
                   : (cached ? kAlgoTwoShotFusedHalfCachedPutsSync : kAlgoTwoShotFusedHalfSync);
@@ -620,7 +637,10 @@ mscl_status_t launch_allreduce(const mscl_channel_s* ch, const KernelArgs& proto
     }
     a.count = c;
     mscl_plan_t sp = plan;
-    if (plan.slices > 1) make_plan(ch, c, dtype, resolved, in_place, &sp, /*allow_slices=*/false);
+    if (plan.slices > 1) {
+      make_plan(ch, c, dtype, resolved, in_place, &sp, /*allow_slices=*/false);
+      sp.cached_puts = plan.cached_puts;  // a slice keeps the whole call's put policy
+    }
     a.chunk = sp.chunk_elems;
     a.nblk = static_cast<uint32_t>(sp.workgroups_per_rank);
     a.xcd_grouped = (resolved == MSCL_ALGO_ONE_SHOT && a.nblk % kXcds == 0) ? 1u : 0u;

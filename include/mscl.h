@@ -110,9 +110,10 @@ typedef struct {
   size_t chunk_elems;        /* two-shot: elements owned by each rank (a multiple of 16/elem_size) */
   int cached_puts;           /* two-shot kernels: 1 when the puts into the outputs are device-scope
                                 temporal stores (the call's 2*R*S bytes fit the Infinity Cache well,
-                                and the outputs stay there for their next reader), 0 when they
-                                stream past the caches.  MSCL_CACHED_PUTS_MAX_BYTES (environment,
-                                read once) replaces the built-in bound on 2*R*S */
+                                and the outputs stay there for their next reader: up to 128 MiB, or
+                                256 MiB for the held two-shot), 0 when they stream past the caches.
+                                MSCL_CACHED_PUTS_MAX_BYTES (environment, read once) replaces the
+                                built-in bounds on 2*R*S */
   int held_tiles;            /* two-shot, R >= 6: reduced tiles per lane each workgroup keeps in LDS
                                 across the barrier instead of storing and re-reading them (its whole
                                 share, 16 to 40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
@@ -250,10 +251,11 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * (see Threading above); MSCL_TWO_SHOT_HOLD=0 (environment, read once)
  * avoids the kernel.
  * Cache policy of the two-shot kernels' puts: when the call's footprint
- * (R inputs + R outputs, 2*R*count*element size) is at most 128 MiB they
- * are device-scope temporal stores, which leave the outputs in the
- * Infinity Cache for the kernel that reads them next; above that they
- * stream past the caches (mscl_channel_plan reports the choice).  It
+ * (R inputs + R outputs, 2*R*count*element size) is at most 128 MiB (256 MiB
+ * for the two-shot that holds its reduced chunk in LDS) they are
+ * device-scope temporal stores, which leave the outputs in the Infinity
+ * Cache for the kernel that reads them next; above that they stream past
+ * the caches (mscl_channel_plan reports the choice).  It
  * changes time only, never results.
  * MSCL_ALGO_TWO_SHOT_PERTILE uses the channels' get (read the peer's memory
  * directly) and a semaphore per tile instead of one barrier (MSCCL++
