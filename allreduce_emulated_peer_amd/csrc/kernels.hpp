@@ -515,12 +515,13 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot(KernelArgs a) {
 // during the all-gather, which writes them to every output, the rank's own
 // included, so the call moves 2*R*S bytes when a workgroup's whole share is
 // held.  Its LDS leaves room for one workgroup per compute unit.  Measured on
-// MI355X, R = 8 bf16, where the host uses it (16 to 40 tiles per workgroup):
+// MI355X, R = 8 bf16, where the host uses it (4 to 40 tiles per workgroup):
 // 16 MiB 44.3 -> 43.3 us, 32 MiB 92.0 -> 87.2 us; R = 16: 16 MiB 93.1 -> 89.2
 // us, 32 MiB 191.2 -> 178.1 us.  Holding part of a larger share gains
-// nothing (R = 8, 128 MiB, 40 of 128 tiles: 375 -> 377 us), and with fewer
-// tiles the all-gather's extra own-output store costs more than it saves
-// (R = 16, 8 MiB, 8 tiles: 47.7 -> 49.0 us).
+// nothing (R = 8, 128 MiB, 40 of 128 tiles: 375 -> 377 us).  With streaming
+// puts, few tiles lost (R = 16, 8 MiB, 8 tiles: 47.7 -> 49.0 us); with
+// device-scope puts they gain (R = 16, 8 MiB: 50-54 -> 44-47 us; R = 6,
+// 4 MiB, 4 tiles: 11.4 -> 10.7 us).
 //
 // kIlv: the tiles of the call are dealt to the ranks in turn instead of one
 // contiguous chunk per rank, so at any moment all workgroups read and write

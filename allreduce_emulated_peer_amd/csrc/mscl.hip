@@ -293,11 +293,19 @@ bool held_cached_puts(int nranks, size_t bytes) {
   return 2 * static_cast<size_t>(nranks) * bytes <= limit;
 }
 
-// Fewest full tiles per workgroup for which the held two-shot pays (below, its
-// all-gather's store of the held tiles to the rank's own output costs more
-// than the skipped store and re-read save: R = 16, 8 MiB, 8 tiles, 47.7 ->
-// 49.0 us; R = 8, 16 MiB, 16 tiles, 44.3 -> 43.3 us).
-constexpr uint64_t kHeldMinTiles = 16;
+// Fewest full tiles per workgroup for which the held two-shot pays.  With
+// device-scope puts (the put policy of calls up to 128-256 MiB of footprint)
+// it pays from 4 tiles (us, unheld -> held, same buffers / four rotated
+// buffer sets / between a producer and a consumer kernel: R = 6, 4 MiB
+// 11.4 / 13.0 / 12.4 -> 10.7 / 12.1 / 11.6; R = 8, 8 MiB 21.5 / 24.0 / 22.4
+// -> 21.2 / 22.6 / 21.7; R = 12, 8 MiB 34.5 / 36.4 / 32.5 -> 31.7 / 36.2 /
+// 20.3); below 4 tiles per workgroup nothing is held.
+constexpr uint64_t kHeldMinTiles = 4;
+
+// Tiles per workgroup a slice of a large held two-shot aims at up to R = 8
+// (R = 8, 128 MiB: slices of 16 tiles 352 us, of 32 tiles 360-364 us, of 8
+// tiles 371 us, as one call 378 us).
+constexpr uint64_t kSliceTiles = 16;
 bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
   if (algo != MSCL_ALGO_TWO_SHOT && algo != MSCL_ALGO_TWO_SHOT_PERTILE && !is_fused(algo)) return false;
   if (bytes > (size_t(1) << 31)) return false;  // the two-shot's buffer store takes a 32-bit byte range
@@ -368,7 +376,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
   plan->workgroups_per_rank = static_cast<int>(b);
   // The two-shot keeps every workgroup's reduced tiles in LDS across the
   // barrier (mscl_twoshot_held) when its whole share fits there and is large
-  // enough to pay for the all-gather's extra store: 16 to kHeldTiles full
+  // enough to pay for the all-gather's extra store: kHeldMinTiles to kHeldTiles full
   // tiles per workgroup, one vector per lane, one workgroup per compute unit,
   // from R = 6 up (R = 5, where AUTO never takes the two-shot, measured
   // 3-4% slower held at 24-40 MiB and 2% faster sliced at 64-128 MiB; R = 6
@@ -393,7 +401,7 @@ void make_plan(const mscl_channel_s* ch, size_t count, int dtype, mscl_algo_t al
       // call 770-815).
       const uint64_t tile_elems = tile * V;
       const uint64_t unit = static_cast<uint64_t>(R) * tile_elems;
-      uint64_t k = R <= 8 ? per_slot / kHeldMinTiles : (per_slot + kHeldTiles - 1) / kHeldTiles;
+      uint64_t k = R <= 8 ? per_slot / kSliceTiles : (per_slot + kHeldTiles - 1) / kHeldTiles;
       for (; k >= 2 && k <= 1024; ++k) {
         const uint64_t m = ((count + k - 1) / k + unit - 1) / unit * unit;
         mscl_plan_t first;

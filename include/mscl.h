@@ -116,7 +116,7 @@ typedef struct {
                                 built-in bounds on 2*R*S */
   int held_tiles;            /* two-shot, R >= 6: reduced tiles per lane each workgroup keeps in LDS
                                 across the barrier instead of storing and re-reading them (its whole
-                                share, 16 to 40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
+                                share, 4 to 40 tiles), 0 when none.  MSCL_TWO_SHOT_HOLD=0 (environment, read once)
                                 turns it off, and the slicing below with it */
   int slices;                /* kernel launches the call runs as: 1, or, for a two-shot too large for its
                                 shares to fit in LDS, consecutive slices of slice_elems elements (the

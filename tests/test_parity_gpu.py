@@ -459,31 +459,36 @@ def test_fused_workgroup_sizes(R, ns, dtype):
     assert seen == {128, 256}
 
 
-@pytest.mark.parametrize("algo", ["two_shot", "two_shot_fused"])
-def test_put_policies_at_the_cache_bound(algo):
-    """The two-shot kernels in both put policies: R = 8 bf16 at 8 MiB per rank
-    (2*R*S = 128 MiB: device-scope puts) and one vector more (streaming puts),
-    out of place and in place, against the oracle."""
-    R, dtype = 8, "bf16"
+@pytest.mark.parametrize("algo,R", [("two_shot", 5), ("two_shot_fused", 8)])
+def test_put_policies_at_the_cache_bound(algo, R):
+    """The two-shot kernels in both put policies, bf16, at the largest size
+    whose 2*R*S bytes fit in 128 MiB (device-scope puts) and one vector more
+    (streaming puts), out of place and in place, against the oracle.  R = 5
+    for the two-shot, which holds nothing in LDS at that rank count (the held
+    kernel has its own, larger bound)."""
+    dtype = "bf16"
     h = G.channel(R)
-    for n, cached in (((8 << 20) // 2, 1), ((8 << 20) // 2 + 8, 0)):
+    n_max = (128 << 20) // (2 * R * 2) // 8 * 8  # whole 16-byte vectors
+    for n, cached in ((n_max, 1), (n_max + 8, 0)):
         xs = P.rand_inputs(R, n, dtype, seed=n % 997)
         want = O.allreduce(xs, dtype)
         for in_place in (False, True):
             plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_CODES[algo], in_place=in_place)
-            assert plan.cached_puts == cached
+            assert plan.cached_puts == cached and plan.held_tiles == 0
             G.note(f"{algo} R={R} n={n} in_place={in_place} cached_puts={cached}")
             outs = G.run(xs, dtype, algo, in_place=in_place)
             G.assert_matches_oracle(outs, want, dtype, f"{algo} n={n} in_place={in_place}")
 
 
 @pytest.mark.parametrize("R,n", [(8, 8 << 20), (8, (8 << 20) + 16384), (8, 12_000_007), (16, 8 << 20),
-                                 (6, 9_000_001), (7, 10_000_003), (12, 8_000_009)],
+                                 (6, 9_000_001), (7, 10_000_003), (12, 8_000_009), (8, 2 << 20),
+                                 (6, 2_500_007), (16, 4_000_037)],
                          ids=["r8_16MiB_cached_puts", "r8_16MiB_plus_one_tile_per_rank", "r8_ragged_24MB",
-                              "r16_16MiB", "r6_ragged", "r7_ragged", "r12_ragged"])
+                              "r16_16MiB", "r6_ragged", "r7_ragged", "r12_ragged", "r8_4MiB_4_tiles",
+                              "r6_ragged_5MB", "r16_ragged_8MB"])
 def test_two_shot_held_in_lds(R, n):
     """The two-shot that keeps each workgroup's reduced tiles in LDS across
-    the barrier (16 to 40 full tiles per workgroup), bf16, out of place and in
+    the barrier (4 to 40 full tiles per workgroup), bf16, out of place and in
     place, against the oracle; the ragged size adds a partial tile and a
     partial vector to the held ones."""
     dtype = "bf16"
@@ -493,7 +498,7 @@ def test_two_shot_held_in_lds(R, n):
     for in_place in (False, True):
         plan = M.channel_plan(h, n, M.BFLOAT16, M.ALGO_TWO_SHOT, in_place=in_place)
         # device-scope puts while the call's 2*R*S bytes fit in 256 MiB, streaming puts above
-        assert 16 <= plan.held_tiles <= 40 and plan.cached_puts == int(2 * R * n * 2 <= (256 << 20))
+        assert 4 <= plan.held_tiles <= 40 and plan.cached_puts == int(2 * R * n * 2 <= (256 << 20))
         G.note(f"two_shot held R={R} n={n} in_place={in_place} held_tiles={plan.held_tiles} "
                f"cached_puts={plan.cached_puts}")
         outs = G.run(xs, dtype, "two_shot", in_place=in_place)
@@ -568,7 +573,7 @@ def test_held_plans_always_hold_whole_shares():
     """The held two-shot serves only workgroups whose whole share fits in LDS
     (it records INVALID_ARGUMENT rather than serve part of one): over a spread
     of ragged sizes at every rank count that holds (R >= 6), every plan (or
-    first slice) with held_tiles > 0 must give its busiest workgroup 16..40
+    first slice) with held_tiles > 0 must give its busiest workgroup 4..40
     full tiles, and slices must cover the call.  Host planning only."""
     g = np.random.default_rng(2026)
     for R in range(6, 17):
@@ -582,7 +587,7 @@ def test_held_plans_always_hold_whole_shares():
                 first = M.channel_plan(h, plan.slice_elems, dtype, M.ALGO_TWO_SHOT)
                 tiles = (first.chunk_elems // V) // 256
                 per_slot = -(-tiles // first.workgroups_per_rank)
-                assert 16 <= per_slot <= 40 and per_slot == plan.held_tiles, (R, n, dtype, per_slot, plan.held_tiles)
+                assert 4 <= per_slot <= 40 and per_slot == plan.held_tiles, (R, n, dtype, per_slot, plan.held_tiles)
                 esize = 2 if dtype == M.BFLOAT16 else 4
                 assert plan.vectors_per_thread == 1 and plan.cached_puts == int(2 * R * n * esize <= (256 << 20))
 
@@ -632,13 +637,22 @@ def test_plan_geometry():
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_AUTO)
     assert q.algo == M.ALGO_TWO_SHOT and q.cached_puts == 1
     q = M.channel_plan(h, mib8 + 8, M.BFLOAT16, M.ALGO_AUTO)
-    assert q.algo == M.ALGO_TWO_SHOT and q.cached_puts == 0
+    # chunks round up to whole 4 KiB pages: 257 tiles over 32 workgroups
+    assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 9 and q.cached_puts == 1  # the held bound: 256 MiB
+    q = M.channel_plan(h, 2 * mib8, M.BFLOAT16, M.ALGO_AUTO)
+    assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 16 and q.cached_puts == 1
+    q = M.channel_plan(h, 2 * mib8 + 8, M.BFLOAT16, M.ALGO_AUTO)
+    assert q.algo == M.ALGO_TWO_SHOT and q.held_tiles == 17 and q.cached_puts == 0
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_AUTO, in_place=True)
     assert q.algo == M.ALGO_TWO_SHOT_FUSED and q.cached_puts == 1 and q.uses_barrier == 1
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_TWO_SHOT_FUSED_NOBARRIER)
     assert q.cached_puts == 1 and q.uses_barrier == 0
     q = M.channel_plan(h, mib8, M.BFLOAT16, M.ALGO_TWO_SHOT)
-    assert q.cached_puts == 1 and q.held_tiles == 0  # 8 tiles per workgroup: too few to hold
+    assert q.cached_puts == 1 and q.held_tiles == 8  # 8 tiles per workgroup, held, device-scope puts
+    q = M.channel_plan(h, (4 << 20) // 2, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.held_tiles == 4  # the fewest held
+    q = M.channel_plan(h, (2 << 20) // 2, M.BFLOAT16, M.ALGO_TWO_SHOT)
+    assert q.held_tiles == 0  # 2 tiles per workgroup: too few to hold
     for algo in (M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT_PORT):  # not a put policy of theirs
         assert M.channel_plan(h, mib8, M.BFLOAT16, algo).cached_puts == 0
     # large chunks are whole 4 KiB pages even when n / R is not; small ones whole 16-byte vectors
