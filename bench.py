@@ -343,7 +343,8 @@ def main() -> int:
         return float(np.median(ts)), K
 
     CTYPE = {"fp32": "F32", "fp16": "F16", "bf16": "BF16"}
-    ALGO_NAME = {1: "one_shot", 2: "two_shot", 3: "two_shot_fused", 4: "two_shot_port", 5: "two_shot_fused_nobarrier"}
+    ALGO_NAME = {1: "one_shot", 2: "two_shot", 3: "two_shot_fused", 4: "two_shot_port", 5: "two_shot_fused_nobarrier",
+                 6: "two_shot_pertile"}
 
     def describe(w, algo=M.ALGO_AUTO, in_place=False):
         """The algorithm, kernel and synchronisation a call of workload `w` runs."""
@@ -354,9 +355,12 @@ def main() -> int:
             kernel = f"mscl_oneshot<{c}, {R}, {'true' if in_place else 'false'}>"
             sync = "after-reads barrier per batch (in place)" if in_place else "none (one-shot)"
         elif p.algo == M.ALGO_TWO_SHOT:
-            kernel = (f"mscl_twoshot_held<{c}, {R}, {'true' if p.tile_interleave else 'false'}>" if p.held_tiles
-                      else f"mscl_twoshot<{c}, {R}, {cached}>")
+            kernel = (f"mscl_twoshot_held<{c}, {R}, {'true' if p.tile_interleave else 'false'}, {cached}>"
+                      if p.held_tiles else f"mscl_twoshot<{c}, {R}, {cached}>")
             sync = "signal/wait barrier between reduce-scatter and all-gather"
+        elif p.algo == M.ALGO_TWO_SHOT_PERTILE:
+            kernel = f"mscl_twoshot_pertile<{c}, {R}, {cached}>"
+            sync = "per-tile semaphores between reduce-scatter and all-gather (labelled variant)"
         elif p.algo == M.ALGO_TWO_SHOT_FUSED:
             kernel = f"mscl_twoshot_fused<{c}, {R}, {p.threads_per_workgroup}, {cached}, true>"
             sync = "completion barrier after the puts"
@@ -389,7 +393,8 @@ def main() -> int:
         f"threads, {plan.vectors_per_thread} vectors/thread, {plan.slices} slice(s) of {plan.slice_elems} elements, "
         f"{plan.held_tiles} tiles held in LDS per workgroup")
     launches = plan.slices  # kernel launches per step (one per slice)
-    main_kernel = (f"mscl_twoshot_held<BF16, {w.nranks}, {'true' if plan.tile_interleave else 'false'}>"
+    main_kernel = (f"mscl_twoshot_held<BF16, {w.nranks}, {'true' if plan.tile_interleave else 'false'}, "
+                   f"{'true' if plan.cached_puts else 'false'}>"
                    if plan.held_tiles else f"mscl_twoshot<BF16, {w.nranks}, false>")
     for _ in range(args.warmup):
         call()
