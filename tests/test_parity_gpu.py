@@ -569,6 +569,53 @@ def test_two_shot_held_fp16(R, n):
         G.assert_matches_oracle(outs, want, dtype, f"held fp16 R={R} n={n} in_place={in_place}")
 
 
+@pytest.mark.parametrize("R,n,dtype,algo", [(8, (8 << 20) // 2 + 24, "bf16", "auto"),
+                                            (8, (64 << 20) // 2, "bf16", "auto"),
+                                            (8, 262_147, "bf16", "two_shot_fused"),
+                                            (4, 4099, "fp32", "one_shot"),
+                                            (6, 1_000_003, "fp16", "two_shot"),
+                                            (16, 2_000_017, "bf16", "two_shot_pertile")],
+                         ids=["r8_held", "r8_held_interleaved_slices", "r8_fused", "r4_one_shot",
+                              "r6_fp16_two_shot", "r16_pertile"])
+def test_buffers_at_16_byte_offsets_in_one_allocation(R, n, dtype, algo):
+    """All 2R buffers carved from one device allocation, each at a random
+    16-byte (not page) aligned offset past the previous one, inputs and
+    outputs alternating: nothing in the kernels may assume more alignment
+    than the 16 bytes the call requires.  Out of place and in place, against
+    the oracle."""
+    G.channel(R)
+    g = np.random.default_rng(n)
+    esize = 4 if dtype == "fp32" else 2
+    nbytes = n * esize
+    offs, o = [], 0
+    for _ in range(2 * R):
+        o += 16 * int(g.integers(1, 256))
+        offs.append(o)
+        o += (nbytes + 15) // 16 * 16
+    big = torch.empty(o + 16, dtype=torch.uint8, device="cuda")
+    assert big.data_ptr() % 16 == 0
+    tdt = G.TORCH_DTYPES[dtype]
+    ins = [big[offs[2 * r]:offs[2 * r] + nbytes].view(tdt) for r in range(R)]
+    outs = [big[offs[2 * r + 1]:offs[2 * r + 1] + nbytes].view(tdt) for r in range(R)]
+    assert all(t.data_ptr() % 16 == 0 for t in ins + outs)
+    assert any(t.data_ptr() % 4096 for t in ins + outs)
+    xs = P.rand_inputs(R, n, dtype, seed=n % 1009)
+    want = G.oracle_full(xs, dtype) if n > (1 << 20) else O.allreduce(xs, dtype)
+    s = torch.cuda.current_stream()
+    for in_place in (False, True):
+        for t, x in zip(ins, xs):
+            t.copy_(G.to_device(x, dtype))
+        dst = ins if in_place else outs
+        if not in_place:
+            for t in outs:
+                t.view(torch.uint8).fill_(G.POISON)
+        G.note(f"carved buffers R={R} n={n} {dtype} {algo} in_place={in_place}")
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in dst], n, G.CODES[dtype], R,
+                    G.ALGOS[algo], s.cuda_stream)
+        s.synchronize()
+        G.assert_matches_oracle_on_device(dst, want, dtype, f"carved {algo} in_place={in_place}")
+
+
 def test_held_plans_always_hold_whole_shares():
     """The held two-shot serves only workgroups whose whole share fits in LDS
     (it records INVALID_ARGUMENT rather than serve part of one): over a spread
