@@ -616,6 +616,40 @@ def test_buffers_at_16_byte_offsets_in_one_allocation(R, n, dtype, algo):
         G.assert_matches_oracle_on_device(dst, want, dtype, f"carved {algo} in_place={in_place}")
 
 
+def test_beyond_32_bit_offsets():
+    """R = 2 bf16 at 2^31 + 13 elements per rank (4 GiB and 26 bytes per
+    buffer), so element indices pass 2^31 and byte offsets 2^32: every
+    algorithm, out of place, and AUTO in place, against the plain-C oracle,
+    compared on the device.  Inputs are small integers drawn in blocks from a
+    seeded generator (so the host finishes them in seconds)."""
+    R, n, dtype = 2, (1 << 31) + 13, "bf16"
+    xs = []
+    for r in range(R):
+        g = np.random.default_rng([20261203, r])
+        x = np.empty(n, dtype=np.uint16)
+        for s0 in range(0, n, 1 << 26):
+            e = min(n, s0 + (1 << 26))
+            v = g.integers(-8, 9, size=e - s0, dtype=np.int8).astype(np.float32)
+            x[s0:e] = (v.view(np.uint32) >> 16).astype(np.uint16)  # small integers: exact in bf16
+        xs.append(x)
+    want = G.to_device(G.oracle_full(xs, dtype), dtype).view(torch.int16)
+    dev_in = [G.to_device(x, dtype) for x in xs]
+    del xs
+    for algo in G.EXPLICIT + ("auto",):
+        plan = M.channel_plan(G.channel(R), n, M.BFLOAT16, G.ALGOS[algo])
+        G.note(f"R=2 bf16 n=2^31+13 {algo} (plan: {plan.workgroups_per_rank} workgroups/rank, "
+               f"{plan.slices} slice(s))")
+        outs = G.run(None, dtype, algo, dev_inputs=dev_in)
+        for r, o in enumerate(outs):
+            assert torch.equal(o.view(torch.int16), want), f"{algo}: output {r} differs from the oracle"
+        del outs
+        torch.cuda.empty_cache()
+    G.note("R=2 bf16 n=2^31+13 auto in place")
+    outs = G.run(None, dtype, "auto", in_place=True, dev_inputs=dev_in)
+    for r, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), want), f"auto in place: output {r} differs from the oracle"
+
+
 def test_held_plans_always_hold_whole_shares():
     """The held two-shot serves only workgroups whose whole share fits in LDS
     (it records INVALID_ARGUMENT rather than serve part of one): over a spread
