@@ -224,7 +224,7 @@ def main() -> int:
             b.record(stream)
         torch.cuda.synchronize()
         t = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
-        return float(np.median(t)), float(t.mean())
+        return float(np.median(t)), float(t.mean()), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
     # Timing-only HIP events: created with hipEventDisableSystemFence, which
     # HIP documents for events used only to measure time (no system-scope
@@ -453,11 +453,12 @@ def main() -> int:
     for lw in (() if args.main_only else (W.sweep_bf16(14), W.integer_small())):
         li = device_inputs(lw)
         lo = [torch.empty_like(t) for t in li]
-        p50, mean = p50_us(caller(lw, li, lo), args.latency_iters)
+        p50, mean, p10, p90 = p50_us(caller(lw, li, lo), args.latency_iters)
         p50_te = p50_us_timing_events(caller(lw, li, lo), args.latency_iters)
         dev_us = graph_us(lw, li, lo)
         b_us = batch_us(caller(lw, li, lo), args.latency_iters)
         latency[f"p50_us_16KiB_{lw.name}"] = round(p50, 2)
+        latency[f"p10_p90_us_16KiB_{lw.name}"] = [round(p10, 2), round(p90, 2)]
         latency[f"p50_us_timing_events_16KiB_{lw.name}"] = round(p50_te, 2)
         latency[f"graph_us_per_call_16KiB_{lw.name}"] = round(dev_us, 2)
         latency[f"batch_us_per_call_16KiB_{lw.name}"] = round(b_us, 2)
@@ -519,7 +520,7 @@ def main() -> int:
         dw = W.decode_bf16()
         di = device_inputs(dw)
         do = [torch.empty_like(t) for t in di]
-        p50, mean = p50_us(caller(dw, di, do), args.latency_iters)
+        p50, mean, p10, p90 = p50_us(caller(dw, di, do), args.latency_iters)
         dev_us = graph_us(dw, di, do)
         # Cold: rotate K buffer sets whose total footprint (K * 2RS = 512 MiB)
         # exceeds the 256 MB Infinity Cache, so every call starts from HBM.
@@ -555,7 +556,8 @@ def main() -> int:
         nob_us = graph_us(dw, di, do, M.ALGO_TWO_SHOT_FUSED_NOBARRIER)
         decode = {"workload": dw.name, **describe(dw),
                   "nobarrier_variant_graph_us_per_call": round(nob_us, 2),
-                  "hot": {"p50_us": round(p50, 2), "p50_us_timing_events": round(p50_te, 2),
+                  "hot": {"p50_us": round(p50, 2), "p10_p90_us": [round(p10, 2), round(p90, 2)],
+                          "p50_us_timing_events": round(p50_te, 2),
                           "graph_us_per_call": round(dev_us, 2),
                           "algbw_GBps_graph": round(dw.bytes_per_rank / dev_us / 1e3, 1),
                           "pct_hbm_peak_graph": round(100 * dw.algorithmic_bytes / dev_us / 1e3 / HBM_PEAK_GBPS, 1),
