@@ -50,7 +50,8 @@
 namespace mscl {
 
 constexpr int kMaxRanks = 16;
-constexpr int kStatusTimeout = 7;  // MSCL_ERR_TIMEOUT
+constexpr int kStatusTimeout = 7;   // MSCL_ERR_TIMEOUT
+constexpr int kStatusProtocol = 8;  // MSCL_ERR_PROTOCOL
 
 // Channel state of one launch, passed by value in the kernel arguments.
 struct ChannelArgs {
@@ -59,10 +60,17 @@ struct ChannelArgs {
   int* status;             // host-mapped status word
   uint32_t slots;          // slot stride of inbound / consumed
   int32_t drop_rank;       // test control: this rank skips signal(); -1 = none
+  int32_t double_rank;     // test control: this rank signals twice each time; -1 = none
+  int32_t check_protocol;  // nonzero: every wait checks the count it reads (kStatusProtocol)
   uint64_t timeout_ticks;  // bound of one wait(), in wall-clock ticks (100 MHz)
   uint32_t* progress;      // [R][slots] per-tile semaphores: tiles each (rank, slot) has finished, all calls
   uint32_t* seen;          // [R][R][slots] the peer's progress a (rank, slot) had consumed before this call
 };
+
+// A semaphore held a count that calls ordered on one stream cannot produce.
+__device__ inline void record_protocol_fault(const ChannelArgs& ch) {
+  __hip_atomic_store(ch.status, kStatusProtocol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // What a barrier orders across ranks (see RankChannels::barrier_all).
 enum class Sync { kPublish, kAfterReads, kAfterWrites, kArrival };
@@ -84,7 +92,8 @@ struct RankChannels {
   // signal(): release-ordered increment of the peer's inbound counter.
   __device__ void signal(int peer) const {
     if (rank == ch.drop_rank) return;
-    __hip_atomic_fetch_add(inbound_of(peer), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(inbound_of(peer), rank == ch.double_rank ? 2u : 1u, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Arrival-only signal: the same increment with no ordering of earlier
@@ -92,7 +101,8 @@ struct RankChannels {
   // peer will not read anything this rank wrote.
   __device__ void signal_arrival(int peer) const {
     if (rank == ch.drop_rank) return;
-    __hip_atomic_fetch_add(inbound_of(peer), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(inbound_of(peer), rank == ch.double_rank ? 2u : 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // flush(): earlier stores complete from this device's point of view.
@@ -100,16 +110,29 @@ struct RankChannels {
 
   // wait(): until the peer's signal count reaches `epoch`; false on timeout.
   // The caller adds the acquire fence when it will read the peer's data.
+  // With ch.check_protocol every count read must lie within one signal of
+  // the epoch: this slot passed its previous barrier only once the peer had
+  // signalled epoch - 1, and the peer cannot signal epoch + 1 before this
+  // slot has signalled it.  A count outside that window means another call,
+  // or a reset, touched the same counters; it is recorded as kStatusProtocol
+  // and the wait goes on as usual.
   __device__ bool wait(int peer, uint32_t epoch) const {
     const uint32_t* c = inbound_from(peer);
-    const uint64_t start = wall_clock64();
-    while (static_cast<int32_t>(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch) < 0) {
-      if (wall_clock64() - start > ch.timeout_ticks) {
-        __hip_atomic_store(ch.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        return false;
+    int32_t d = static_cast<int32_t>(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch);
+    if (d < 0) {
+      const uint64_t start = wall_clock64();
+      while (true) {
+        if (ch.check_protocol && d < -1) record_protocol_fault(ch);
+        if (wall_clock64() - start > ch.timeout_ticks) {
+          __hip_atomic_store(ch.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        d = static_cast<int32_t>(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch);
+        if (d >= 0) break;
       }
-      __builtin_amdgcn_s_sleep(1);
     }
+    if (ch.check_protocol && d > 1) record_protocol_fault(ch);
     return true;
   }
 
@@ -203,22 +226,38 @@ struct TileSemaphores {
   // increment already promises the peers that the tile's data is complete.
   __device__ void signal_tile() const {
     if (rank == ch.drop_rank) return;
-    __hip_atomic_fetch_add(progress_of(rank), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(progress_of(rank), rank == ch.double_rank ? 2u : 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // With ch.check_protocol: a peer's count of finished tiles in this call
+  // lies between 0 and the `total` tiles its slot signals in the call;
+  // anything else is recorded as kStatusProtocol.
+  __device__ void check_tiles(uint32_t have, uint32_t total) const {
+    if (ch.check_protocol && (static_cast<int32_t>(have) < 0 || have > total)) record_protocol_fault(ch);
   }
 
   // Tiles of this call peer p's slot has finished (progress - base), polled
-  // until at least `need`.  On running out of time the status records TIMEOUT
-  // and every tile of the peer is reported finished, so the caller waits for
-  // that peer at most once per call (its outputs are then wrong).
-  __device__ uint32_t wait_tiles(int p, uint32_t base, uint32_t need) const {
+  // until at least `need` (of `total`).  On running out of time the status
+  // records TIMEOUT and every tile of the peer is reported finished, so the
+  // caller waits for that peer at most once per call (its outputs are then
+  // wrong).
+  __device__ uint32_t wait_tiles(int p, uint32_t base, uint32_t need, uint32_t total) const {
     const uint32_t* c = progress_of(p);
     uint32_t have = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
-    if (static_cast<int32_t>(have - need) >= 0) return have;
+    if (static_cast<int32_t>(have - need) >= 0) {
+      check_tiles(have, total);
+      return have;
+    }
     const uint64_t start = wall_clock64();
     while (true) {
+      check_tiles(have, total);
       __builtin_amdgcn_s_sleep(1);
       have = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
-      if (static_cast<int32_t>(have - need) >= 0) return have;
+      if (static_cast<int32_t>(have - need) >= 0) {
+        check_tiles(have, total);
+        return have;
+      }
       if (wall_clock64() - start > ch.timeout_ticks) {
         __hip_atomic_store(ch.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         return 0x7FFFFFFFu;

@@ -792,16 +792,18 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_pertile(KernelArgs a) {
   // of peer p's tiles are known finished (first from one read of every
   // peer's semaphore, lane p of wave 0 reading peer p's), so a semaphore is
   // polled again only when the tile needed next is not yet known finished.
-  __shared__ uint32_t base_sh[kMaxRanks], ready_sh[kMaxRanks], nvec_sh[kMaxRanks];
+  __shared__ uint32_t base_sh[kMaxRanks], ready_sh[kMaxRanks], nvec_sh[kMaxRanks], total_sh[kMaxRanks];
   if (lane < static_cast<uint32_t>(R)) {
     const int p = static_cast<int>(lane);
     const Chunk gp = chunk_of<C, U>(a, p, slot);
     const uint64_t nfull_mine = static_cast<uint64_t>(slot) < gp.nfull_tiles ? (gp.nfull_tiles - 1 - slot) / B + 1 : 0;
     nvec_sh[p] = p == rank ? 0u : static_cast<uint32_t>(nfull_mine + (gp.owns_partial_tile ? 1 : 0));
+    total_sh[p] = p == rank ? 0u : slot_tiles<C, U>(gp, slot, B);
     const uint32_t b0 = __hip_atomic_load(sem.seen_of(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     base_sh[p] = b0;
     const uint32_t have =
         p == rank ? 0u : __hip_atomic_load(sem.progress_of(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - b0;
+    sem.check_tiles(have, total_sh[p]);
     ready_sh[p] = static_cast<int32_t>(have) > 0 ? have : 0u;
   }
   __syncthreads();
@@ -812,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_pertile(KernelArgs a) {
     if (lane == 0) {
       for (int k = 1; k < R; ++k) {
         const int p = (rank + k) % R;
-        if (j < nvec_sh[p] && j >= ready_sh[p]) ready_sh[p] = sem.wait_tiles(p, base_sh[p], j + 1);
+        if (j < nvec_sh[p] && j >= ready_sh[p]) ready_sh[p] = sem.wait_tiles(p, base_sh[p], j + 1, total_sh[p]);
       }
     }
     __syncthreads();
@@ -854,7 +856,7 @@ __global__ __launch_bounds__(kThreads) void mscl_twoshot_pertile(KernelArgs a) {
       if (p == rank) continue;
       const Chunk gp = chunk_of<C, U>(a, p, slot);
       if (gp.ntail == 0) continue;
-      if (ready_sh[p] < nvec_sh[p] + 1) sem.wait_tiles(p, base_sh[p], nvec_sh[p] + 1);
+      if (ready_sh[p] < nvec_sh[p] + 1) sem.wait_tiles(p, base_sh[p], nvec_sh[p] + 1, total_sh[p]);
       store_partial<C>(mine, gp.v_full, load_partial_scoped<C, kBufferSc1>(a.out[p], gp.v_full, gp.ntail), gp.ntail);
     }
   }

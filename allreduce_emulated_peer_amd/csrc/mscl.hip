@@ -85,6 +85,7 @@ struct Config {
   bool two_shot_hold;                // the two-shot may keep reduced tiles in LDS (mscl_twoshot_held)
   bool tile_interleave;              // whole-R-tile held slices deal tiles to the ranks in turn
   int log_level;                     // MSCL_LOG: 0..3
+  bool check_protocol;               // MSCL_CHECK_PROTOCOL: channel sets start with their waits checking counts
 };
 
 const Config& config() {
@@ -98,6 +99,7 @@ const Config& config() {
     c.two_shot_hold = env_size("MSCL_TWO_SHOT_HOLD", 1) != 0;
     c.tile_interleave = env_size("MSCL_TILE_INTERLEAVE", 1) != 0;
     c.log_level = static_cast<int>(std::min<size_t>(env_size("MSCL_LOG", 0), 3));
+    c.check_protocol = env_size("MSCL_CHECK_PROTOCOL", 0) != 0;
     // clamped to a day, so the microsecond count (and its tick count) cannot wrap
     c.wait_timeout_us = std::min<size_t>(env_size("MSCL_WAIT_TIMEOUT_MS", 2000), size_t(86400000)) * 1000;
   });
@@ -135,6 +137,8 @@ struct mscl_channel_s {
   int* status_dev = nullptr;
   uint64_t wait_timeout_us = 0;  // 0 = config default
   int drop_rank = -1;
+  int double_rank = -1;          // test control: this rank signals twice each time
+  int check_protocol = 0;        // waits check the counts they read (MSCL_ERR_PROTOCOL)
   mscl::proxy::PortState* port = nullptr;  // started by the first port-channel call
 };
 
@@ -433,6 +437,8 @@ struct Bound {
   mscl_channel_s* ch = nullptr;
   uint64_t timeout_us = 0;
   int drop_rank = -1;
+  int double_rank = -1;
+  int check_protocol = 0;
 };
 
 // SUCCESS, or the failure an earlier call recorded in the set's status word
@@ -457,6 +463,8 @@ mscl_status_t bind_channel(int nranks, Bound* b) {
     b->ch = it->second;
     b->timeout_us = b->ch->wait_timeout_us ? b->ch->wait_timeout_us : config().wait_timeout_us;
     b->drop_rank = b->ch->drop_rank;
+    b->double_rank = b->ch->double_rank;
+    b->check_protocol = b->ch->check_protocol;
   }
   return recorded_failure(b->ch);
 }
@@ -476,6 +484,8 @@ void fill_args(KernelArgs* a, const Bound& b, const void* const inputs[], void* 
   a->ch.status = b.ch->status_dev;
   a->ch.slots = b.ch->slots;
   a->ch.drop_rank = b.drop_rank;
+  a->ch.double_rank = b.double_rank;
+  a->ch.check_protocol = b.check_protocol;
   a->ch.timeout_ticks = b.timeout_us * b.ch->wall_clock_khz / 1000;
 }
 
@@ -745,6 +755,7 @@ const char* mscl_status_string(mscl_status_t s) {
     case MSCL_ERR_OUT_OF_MEMORY: return "out of memory";
     case MSCL_ERR_HIP: return "HIP runtime error";
     case MSCL_ERR_TIMEOUT: return "device-side wait timed out";
+    case MSCL_ERR_PROTOCOL: return "a semaphore count that ordered calls cannot produce (overlapping calls on one channel set?)";
   }
   return "unknown status";
 }
@@ -796,6 +807,7 @@ mscl_status_t mscl_channel_create(int nranks, int device, mscl_channel_t* out) {
   ch->device = device;
   ch->nranks = nranks;
   ch->refcount = 1;
+  ch->check_protocol = config().check_protocol ? 1 : 0;
   ch->cus = prop.multiProcessorCount;
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
@@ -894,6 +906,16 @@ mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t ch, uint64_t wait_t
   return MSCL_SUCCESS;
 }
 
+mscl_status_t mscl_channel_set_checks(mscl_channel_t ch, int check_protocol, int double_signal_rank) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!ch || !registered(ch)) return fail(MSCL_ERR_INVALID_ARGUMENT, "unknown channel handle");
+  if (double_signal_rank < -1 || double_signal_rank >= ch->nranks)
+    return fail(MSCL_ERR_INVALID_ARGUMENT, "double_signal_rank must be -1 or a rank");
+  ch->check_protocol = check_protocol ? 1 : 0;
+  ch->double_rank = double_signal_rank;
+  return MSCL_SUCCESS;
+}
+
 mscl_status_t mscl_channel_plan(mscl_channel_t ch, size_t count, mscl_dtype_t dtype, mscl_algo_t algo,
                                 int in_place, mscl_plan_t* plan) {
   if (!plan) return fail(MSCL_ERR_INVALID_ARGUMENT, "plan is null");
@@ -969,6 +991,8 @@ mscl_status_t mscl_allreduce_noalloc(const void* const inputs[], void* const out
   a.ch.status = reinterpret_cast<int*>(d.scratch + words - 1);
   a.ch.slots = stride;
   a.ch.drop_rank = -1;
+  a.ch.double_rank = -1;
+  a.ch.check_protocol = config().check_protocol ? 1 : 0;
   a.ch.timeout_ticks = config().wait_timeout_us * d.wall_clock_khz / 1000;
   if (plan.uses_barrier) {
     void* kargs[] = {&d.scratch, &words};
@@ -1019,6 +1043,8 @@ mscl_status_t mscl_channel_selftest(mscl_channel_t ch, uint32_t rounds, uint64_t
     b.ch = ch;
     b.timeout_us = ch->wait_timeout_us ? ch->wait_timeout_us : config().wait_timeout_us;
     b.drop_rank = ch->drop_rank;
+    b.double_rank = ch->double_rank;
+    b.check_protocol = ch->check_protocol;
   }
   if (const mscl_status_t st = recorded_failure(ch); st != MSCL_SUCCESS) return st;
   if (rounds == 0) return MSCL_SUCCESS;

@@ -32,6 +32,7 @@ ERR_NOT_INITIALIZED = 4
 ERR_OUT_OF_MEMORY = 5
 ERR_HIP = 6
 ERR_TIMEOUT = 7
+ERR_PROTOCOL = 8
 
 DTYPE_CODES = {"fp32": FLOAT32, "fp16": FLOAT16, "bf16": BFLOAT16}
 ALGO_CODES = {"auto": ALGO_AUTO, "one_shot": ALGO_ONE_SHOT, "two_shot": ALGO_TWO_SHOT,
@@ -42,8 +43,8 @@ ALGO_CODES = {"auto": ALGO_AUTO, "one_shot": ALGO_ONE_SHOT, "two_shot": ALGO_TWO
 EXPORTS = (
     "mscl_version", "mscl_status_string", "mscl_last_error_string", "mscl_channel_create",
     "mscl_channel_destroy", "mscl_channel_check", "mscl_channel_reset", "mscl_allreduce",
-    "mscl_select_algo", "mscl_channel_plan", "mscl_channel_set_fault_controls", "mscl_reduce_scatter",
-    "mscl_allgather", "mscl_channel_selftest", "mscl_allreduce_noalloc",
+    "mscl_select_algo", "mscl_channel_plan", "mscl_channel_set_fault_controls", "mscl_channel_set_checks",
+    "mscl_reduce_scatter", "mscl_allgather", "mscl_channel_selftest", "mscl_allreduce_noalloc",
 )
 
 
@@ -107,6 +108,8 @@ def load(path: str = LIB_PATH):
     lib.mscl_channel_plan.argtypes = [vp, c_size, c_int, c_int, c_int, ctypes.POINTER(Plan)]
     lib.mscl_channel_set_fault_controls.restype = c_int
     lib.mscl_channel_set_fault_controls.argtypes = [vp, ctypes.c_uint64, c_int]
+    lib.mscl_channel_set_checks.restype = c_int
+    lib.mscl_channel_set_checks.argtypes = [vp, c_int, c_int]
     _lib = lib
     return lib
 
@@ -192,7 +195,7 @@ def channel_destroy(handle: int) -> None:
 
 
 def channel_check(handle: int) -> int:
-    """Status recorded on the device by earlier calls (SUCCESS or ERR_TIMEOUT)."""
+    """Status recorded on the device by earlier calls (SUCCESS, ERR_TIMEOUT, ERR_PROTOCOL, ...)."""
     return load().mscl_channel_check(ctypes.c_void_p(handle))
 
 
@@ -203,6 +206,13 @@ def channel_reset(handle: int) -> None:
 def channel_set_fault_controls(handle: int, wait_timeout_us: int = 0, drop_signal_rank: int = -1) -> None:
     _check(load().mscl_channel_set_fault_controls(ctypes.c_void_p(handle), wait_timeout_us, drop_signal_rank),
            "mscl_channel_set_fault_controls")
+
+
+def channel_set_checks(handle: int, check_protocol: bool = True, double_signal_rank: int = -1) -> None:
+    """mscl_channel_set_checks: protocol checks of every device-side wait, and
+    the test control that makes one rank signal twice."""
+    _check(load().mscl_channel_set_checks(ctypes.c_void_p(handle), int(bool(check_protocol)), double_signal_rank),
+           "mscl_channel_set_checks")
 
 
 def channel_selftest(handle: int, rounds: int) -> int:

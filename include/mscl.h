@@ -96,6 +96,8 @@ typedef int mscl_status_t;
 #define MSCL_ERR_OUT_OF_MEMORY 5    /* channel state could not be allocated */
 #define MSCL_ERR_HIP 6              /* a HIP runtime call or kernel launch failed */
 #define MSCL_ERR_TIMEOUT 7          /* a device-side wait() ran out of time */
+#define MSCL_ERR_PROTOCOL 8         /* with protocol checks on (mscl_channel_set_checks): a semaphore held a
+                                       count that calls ordered on one stream cannot produce */
 
 typedef struct mscl_channel_s* mscl_channel_t;
 
@@ -186,7 +188,8 @@ mscl_status_t mscl_channel_destroy(mscl_channel_t channel);
 
 /*
  * Report a failure recorded by an earlier call on this set: a wait() that
- * ran out of time (TIMEOUT), or a port-channel request the proxy refused
+ * ran out of time (TIMEOUT), a semaphore count that ordered calls cannot
+ * produce (PROTOCOL, with mscl_channel_set_checks), or a port-channel request the proxy refused
  * (INVALID_ARGUMENT: a range outside the device allocations) or could not
  * issue (HIP).  The pages' wait() blocks until the peer signals (MSCCL++
  * README, Key Concepts, "On-GPU Communication Interfaces: Channels") and are
@@ -274,7 +277,7 @@ mscl_status_t mscl_channel_reset(mscl_channel_t channel);
  * device allocations before copying and records INVALID_ARGUMENT for one
  * that leaves them.  Each put costs the copy engines ~20 us of set-up, so
  * this algorithm is for moving data without compute units, not for speed.
- * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, PROTOCOL, HIP.
  */
 mscl_status_t mscl_allreduce(const void* const inputs[], void* const outputs[], size_t count,
                              mscl_dtype_t dtype, int nranks, mscl_algo_t algo, void* stream);
@@ -321,7 +324,7 @@ mscl_status_t mscl_allreduce_noalloc(const void* const inputs[], void* const out
  * aligned the data moves as 16-byte vectors, otherwise element by element.
  * Each rank gets its block from every peer and writes only its own output, so
  * the call runs no barrier.  Asynchronous, one kernel, no allocation.
- * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, PROTOCOL, HIP.
  */
 mscl_status_t mscl_reduce_scatter(const void* const inputs[], void* const outputs[], size_t recvcount,
                                   mscl_dtype_t dtype, int nranks, void* stream);
@@ -344,7 +347,7 @@ mscl_status_t mscl_reduce_scatter(const void* const inputs[], void* const output
  * the call's completion on the stream is the completion point.
  * Pointers need element-size alignment (16-byte vectors when every block
  * boundary allows).  Asynchronous, one kernel, no allocation.
- * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, HIP.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, NOT_INITIALIZED, TIMEOUT, PROTOCOL, HIP.
  */
 mscl_status_t mscl_allgather(const void* const inputs[], void* const outputs[], size_t sendcount,
                              mscl_dtype_t dtype, int nranks, void* stream);
@@ -398,6 +401,31 @@ mscl_status_t mscl_channel_plan(mscl_channel_t channel, size_t count, mscl_dtype
  */
 mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t channel, uint64_t wait_timeout_us,
                                               int drop_signal_rank);
+
+/*
+ * Protocol checks, a race detector for the concurrency contract above (the
+ * pages are silent on it; the counters are this library's semaphores).
+ *   check_protocol    : nonzero makes every device-side wait of later calls on
+ *                       this set check the count it reads.  A barrier wait
+ *                       for epoch e can only ever see e - 1, e or e + 1 from
+ *                       calls ordered on one stream (the peer cannot signal
+ *                       e + 1 before this slot signals e, nor this slot wait
+ *                       for e before the peer reached e - 1); a per-tile wait
+ *                       only counts between 0 and the tiles the peer signals
+ *                       in the call.  Any other count (two calls overlapping
+ *                       on one set, a reset while a call ran) is recorded as
+ *                       MSCL_ERR_PROTOCOL in the status word, reported like
+ *                       TIMEOUT, and the call carries on.  Costs a compare per
+ *                       wait.  MSCL_CHECK_PROTOCOL=1 (environment, read once)
+ *                       turns it on for every new channel set.
+ *   double_signal_rank: test control, -1 for normal operation; r in 0..R-1
+ *                       makes rank r signal every barrier and every tile
+ *                       twice, as a second call on the same counters would,
+ *                       so that the checks have something to find.  No wait
+ *                       blocks longer than without it.
+ * Errors: INVALID_ARGUMENT (unknown handle, double_signal_rank out of range).
+ */
+mscl_status_t mscl_channel_set_checks(mscl_channel_t channel, int check_protocol, int double_signal_rank);
 
 /*
  * Check the channel contract on the device (for tests and bring-up; it

@@ -43,7 +43,7 @@ def test_missing_library_fails_loudly(tmp_path):
 
 def test_version_and_strings():
     assert M.version() == 100
-    for code in range(8):
+    for code in range(9):
         assert M.status_string(code) != "unknown status"
     assert M.status_string(99) == "unknown status"
 
@@ -155,6 +155,8 @@ def test_channel_calls_reject_unknown_handles():
     assert lib.mscl_channel_check(bogus) == M.ERR_INVALID_ARGUMENT
     assert lib.mscl_channel_reset(bogus) == M.ERR_INVALID_ARGUMENT
     assert lib.mscl_channel_set_fault_controls(bogus, 0, -1) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_set_checks(bogus, 1, -1) == M.ERR_INVALID_ARGUMENT
+    assert lib.mscl_channel_set_checks(None, 0, -1) == M.ERR_INVALID_ARGUMENT
     plan = M.Plan()
     assert lib.mscl_channel_plan(bogus, 10, 0, 0, 0, ctypes.byref(plan)) == M.ERR_INVALID_ARGUMENT
     count = ctypes.c_uint64()
