@@ -69,6 +69,8 @@ int main(void) {
   expect("reset", mscl_channel_reset(bogus), MSCL_ERR_INVALID_ARGUMENT);
   expect("plan", mscl_channel_plan(bogus, 10, MSCL_FLOAT32, MSCL_ALGO_AUTO, 0, &plan), MSCL_ERR_INVALID_ARGUMENT);
   expect("faults", mscl_channel_set_fault_controls(bogus, 0, -1), MSCL_ERR_INVALID_ARGUMENT);
+  expect("checks", mscl_channel_set_checks(bogus, 1, -1), MSCL_ERR_INVALID_ARGUMENT);
+  expect("checks null", mscl_channel_set_checks(NULL, 0, -1), MSCL_ERR_INVALID_ARGUMENT);
   expect("selftest", mscl_channel_selftest(bogus, 1, &mism), MSCL_ERR_INVALID_ARGUMENT);
   mscl_channel_t h;
   expect("create R 0", mscl_channel_create(0, 0, &h), MSCL_ERR_INVALID_ARGUMENT);
