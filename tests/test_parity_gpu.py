@@ -552,21 +552,23 @@ def test_held_planner_edges(extra_tiles, tail):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("R,n", [(8, 12_000_007), (8, 24_000_017), (16, 9_000_011)],
-                         ids=["r8_held", "r8_sliced", "r16_held"])
-def test_two_shot_held_fp16(R, n):
-    """The held two-shot (one launch or slices) on fp16, with a ragged tail,
-    out of place and in place, against the oracle."""
-    dtype = "fp16"
+@pytest.mark.parametrize("R,n,dtype", [(8, 12_000_007, "fp16"), (8, 24_000_017, "fp16"), (16, 9_000_011, "fp16"),
+                                       (8, 1 << 20, "fp32"), (6, 1_250_003, "fp32"), (12, 40_000_003, "fp32")],
+                         ids=["r8_held", "r8_sliced", "r16_held", "r8_fp32_4_tiles", "r6_fp32_ragged",
+                              "r12_fp32_sliced"])
+def test_two_shot_held_fp16_fp32(R, n, dtype):
+    """The held two-shot (one launch or slices) on fp16 and fp32, from the
+    fewest held tiles (4) to slices, with ragged tails, out of place and in
+    place, against the oracle."""
     h = G.channel(R)
     xs = P.rand_inputs(R, n, dtype, seed=n % 967)
     want = G.oracle_full(xs, dtype)
     for in_place in (False, True):
-        plan = M.channel_plan(h, n, M.FLOAT16, M.ALGO_TWO_SHOT, in_place=in_place)
-        assert 16 <= plan.held_tiles <= 40
-        G.note(f"two_shot held fp16 R={R} n={n} in_place={in_place} slices={plan.slices} held={plan.held_tiles}")
+        plan = M.channel_plan(h, n, G.CODES[dtype], M.ALGO_TWO_SHOT, in_place=in_place)
+        assert 4 <= plan.held_tiles <= 40
+        G.note(f"two_shot held {dtype} R={R} n={n} in_place={in_place} slices={plan.slices} held={plan.held_tiles}")
         outs = G.run(xs, dtype, "two_shot", in_place=in_place)
-        G.assert_matches_oracle(outs, want, dtype, f"held fp16 R={R} n={n} in_place={in_place}")
+        G.assert_matches_oracle(outs, want, dtype, f"held {dtype} R={R} n={n} in_place={in_place}")
 
 
 @pytest.mark.parametrize("R,n,dtype,algo", [(8, (8 << 20) // 2 + 24, "bf16", "auto"),
