@@ -310,7 +310,6 @@ constexpr uint64_t kHeldMinTiles = 4;
 // (R = 8, 128 MiB: slices of 16 tiles 352 us, of 32 tiles 360-364 us, of 8
 // tiles 371 us, as one call 378 us).
 constexpr uint64_t kSliceTiles = 16;
-
 bool cached_puts(mscl_algo_t algo, int nranks, size_t bytes) {
   if (algo != MSCL_ALGO_TWO_SHOT && algo != MSCL_ALGO_TWO_SHOT_PERTILE && !is_fused(algo)) return false;
   if (bytes > (size_t(1) << 31)) return false;  // the two-shot's buffer store takes a 32-bit byte range
