@@ -423,6 +423,8 @@ mscl_status_t mscl_channel_set_fault_controls(mscl_channel_t channel, uint64_t w
  *                       twice, as a second call on the same counters would,
  *                       so that the checks have something to find.  No wait
  *                       blocks longer than without it.
+ * Both settings stay until changed; mscl_channel_reset clears the recorded
+ * status and the counters, not these.
  * Errors: INVALID_ARGUMENT (unknown handle, double_signal_rank out of range).
  */
 mscl_status_t mscl_channel_set_checks(mscl_channel_t channel, int check_protocol, int double_signal_rank);
