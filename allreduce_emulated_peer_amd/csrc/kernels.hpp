@@ -26,6 +26,12 @@
 //                       straight into every output as device-scope puts,
 //                       then a completion barrier (or, as an explicitly
 //                       requested variant, no barrier).
+//   mscl_twoshot_pertile
+//                       reduce-scatter that signals every finished tile on a
+//                       per-tile semaphore, and an all-gather that gets each
+//                       peer's tile as soon as its semaphore shows it.
+//   mscl_twoshot_port   reduce-scatter, then all-gather puts posted to a host
+//                       proxy that copies them with the DMA engines.
 //   mscl_reduce_scatter_kernel / mscl_allgather_kernel
 //                       the two halves as standard collectives.
 //   mscl_channel_selftest_kernel
@@ -41,9 +47,11 @@
 // small messages); a tile is U 16-byte vectors per lane.
 //
 // Two-shot chunks: rank r owns elements [r*c, min((r+1)*c, n)) with
-// c = roundup(ceil(n/R), V), V = 16 / element size.  Each lane handles the
-// same vectors in both phases, which keeps in-place calls safe: the only
-// reader of in[p][chunk r] is rank r itself, earlier, in the same lane.
+// c = roundup(ceil(n/R), V), V = 16 / element size (rounded up to whole
+// 4 KiB pages for large chunks; the slices of large held calls instead deal
+// whole tiles to the ranks in turn).  Each lane handles the same vectors in
+// both phases, which keeps in-place calls safe: the only reader of
+// in[p][chunk r] is rank r itself, earlier, in the same lane.
 //
 // Every reduction adds in rank order 0..R-1 starting from rank 0's value and
 // rounds once, so all algorithms give bit-identical results.
