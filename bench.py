@@ -601,7 +601,8 @@ def main() -> int:
         size_curve = {"note": "R=8 bf16, AUTO's pick; us per call from graph replay: hot = same buffers every call, "
                               "cold = buffer sets rotated so that the replayed footprint reaches 512 MiB (K sets); "
                               "pct_hbm_peak = 2RS/t over 8 TB/s; cache_resident: the hot call's 2RS fits the 256 MB "
-                              "Infinity Cache, so only its cold figure measures HBM"}
+                              "Infinity Cache, so only its cold figure measures HBM; *_variant_hot_us: labelled "
+                              "variants AUTO never picks (fused without its barrier, per-tile semaphores)"}
         for k in range(19, 28):
             cw = W.sweep_bf16(k)
             ci_ = device_inputs(cw)
@@ -620,6 +621,8 @@ def main() -> int:
             if entry["algo"] == "two_shot_fused":
                 entry["nobarrier_variant_hot_us"] = round(
                     graph_us(cw, ci_, co_, M.ALGO_TWO_SHOT_FUSED_NOBARRIER, reps), 2)
+            if k in (19, 22, 26):  # the per-tile-semaphore variant beside AUTO's pick (hot)
+                entry["pertile_variant_hot_us"] = round(graph_us(cw, ci_, co_, M.ALGO_TWO_SHOT_PERTILE, reps), 2)
             size_curve[f"{cw.bytes_per_rank}B"] = entry
             del ci_, co_
             torch.cuda.empty_cache()
