@@ -108,3 +108,39 @@ def test_doubled_signals_are_caught(algo, in_place, n):
     torch.cuda.synchronize()
     assert M.channel_check(h) == M.SUCCESS
     M.channel_set_checks(h, False, -1)
+
+
+def test_environment_turns_checks_on_for_new_sets_and_the_noalloc_entry():
+    """MSCL_CHECK_PROTOCOL=1 (read once per process) starts every channel set
+    with the checks on: a child process runs ordered calls of every waiting
+    algorithm and must see no failure recorded.  The allocation-free entry
+    point runs its kernels with the checks on too, between those calls (its
+    status word is device-only, so it can only show here as a call that does
+    not return or a channel set that records something)."""
+    import os
+    import subprocess
+    import sys
+
+    code = r"""
+import torch
+from allreduce_emulated_peer_amd import mscl as M
+dev = torch.cuda.current_device()
+h = M.channel_create(8, dev)
+for n in (4099, 262147, 4194311, (64 << 20) // 2):
+    ins = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(8)]
+    outs = [torch.empty_like(t) for t in ins]
+    s = torch.cuda.current_stream().cuda_stream
+    for algo in (M.ALGO_AUTO, M.ALGO_ONE_SHOT, M.ALGO_TWO_SHOT, M.ALGO_TWO_SHOT_FUSED, M.ALGO_TWO_SHOT_PERTILE):
+        M.allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, 8, algo, s)
+        if n <= 262147:
+            M.allreduce_noalloc([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], n, M.BFLOAT16, 8, algo, s)
+    torch.cuda.synchronize()
+    assert M.channel_check(h) == M.SUCCESS, M.status_string(M.channel_check(h))
+print("checks on, nothing recorded", flush=True)
+"""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MSCL_CHECK_PROTOCOL="1", PYTHONPATH=root)
+    G.note("child process with MSCL_CHECK_PROTOCOL=1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "nothing recorded" in r.stdout
